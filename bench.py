@@ -1,0 +1,293 @@
+"""Benchmark of the fused all-reduce core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one ar_residual_rmsnorm call on the large fused workload: 8 bf16
+rank partials of [2048 tokens, 8192 hidden] summed in fp32, plus residual, then
+RMSNorm (eps 1e-5, no bias), writing the pre-norm sum and the normed output.
+Inputs are seeded synthetic data already resident in HBM. Steps rotate over
+several copies of the inputs so that each call streams from HBM rather than
+from the 256 MB last-level cache.
+
+Prints ONE JSON line: effective HBM GB/s (algorithmic bytes / time), the
+roofline of the fused kernel against the 8 TB/s HBM peak, the standalone sum
+on its large workload, a copy-kernel ceiling, and the CPU oracle timed on the
+host (its own baseline, single-threaded).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s and % of peak, fused AR+residual+RMSNorm, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+LLC_BYTES = 256 << 20   # MI355X Infinity Cache
+FUSED_KERNEL = "ar_rmsnorm_pack_kernel"
+SUM_KERNEL = "ar_sum_pack_kernel"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="fused workload name (default: the large bf16 one)")
+    ap.add_argument("--no-sum", action="store_true", help="skip the standalone-sum line item")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (repeats the sample)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("tensor_all_reduce_ar_amd/csrc/ar.hip", "include/ar.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(f"{kernel}:{workload}")
+    if not entry or entry.get("source_hash") != source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def rotation_sets(bytes_per_set: int) -> int:
+    # enough copies that the cycle is more than twice the last-level cache
+    return max(2, -(-2 * LLC_BYTES // bytes_per_set) + 1)
+
+
+def time_launches(torch, launch, nsets, steps, warmup, stream):
+    """Whole-region timing (ms per step) and per-launch kernel timing (ms),
+    both with HIP events on the launch stream."""
+    for i in range(warmup):
+        launch(i % nsets)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        launch(i % nsets)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    region_ms = start.elapsed_time(stop)
+    # per-launch events: the average duration of one kernel launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        launch(i % nsets)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    return region_ms / steps, statistics.mean(per), statistics.median(per), min(per)
+
+
+def dev(torch, a, dtype):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def bench_fused(torch, ar, w, args, stream):
+    nb = w.algorithmic_bytes()
+    nsets = rotation_sets(nb)
+    base = [dev(torch, p, w.dtype) for p in w.partials]
+    res0 = dev(torch, w.residual, w.dtype)
+    weight = dev(torch, w.weight, w.dtype)
+    bias = dev(torch, w.bias, w.dtype) if w.bias is not None else None
+    sets = []
+    for k in range(nsets):
+        parts = base if k == 0 else [p.clone() for p in base]
+        res = res0 if k == 0 else res0.clone()
+        sets.append((parts, res, torch.empty_like(res0), torch.empty_like(res0)))
+
+    def launch(k):
+        parts, res, out, inter = sets[k]
+        ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res, stream=stream)
+
+    ms_step, k_mean, k_med, k_min = time_launches(torch, launch, nsets, args.steps, args.warmup, stream)
+    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, k_mean=k_mean, k_med=k_med, k_min=k_min,
+                out=sets[0][2], inter=sets[0][3])
+
+
+def bench_sum(torch, ar, w, args, stream):
+    nb = w.algorithmic_bytes()
+    nsets = rotation_sets(nb)
+    base = [dev(torch, p, w.dtype) for p in w.partials]
+    sets = []
+    for k in range(nsets):
+        parts = base if k == 0 else [p.clone() for p in base]
+        sets.append((parts, torch.empty_like(base[0])))
+
+    def launch(k):
+        ar.ar_sum(sets[k][0], sets[k][1], stream=stream)
+
+    steps = max(5, args.steps // 2)
+    ms_step, k_mean, k_med, k_min = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
+    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, k_mean=k_mean, k_med=k_med, k_min=k_min, steps=steps)
+
+
+def copy_ceiling(torch, stream):
+    """A plain device copy of 1 GiB: read + write bytes over time."""
+    n = 1 << 28  # fp32 elements, 1 GiB
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 10
+    del src, dst
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(w, seconds):
+    """The CPU oracle (single-threaded C) on the same inputs, repeated over the
+    whole workload until `seconds` have passed (at least once)."""
+    import numpy as np
+
+    import oracle
+    out = np.zeros(w.n, dtype=w.partials[0].dtype)
+    inter = np.zeros(w.n, dtype=w.partials[0].dtype)
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        oracle.ar_residual_rmsnorm(w.dtype, w.partials, w.hidden, w.weight, w.eps, out, inter, bias=w.bias,
+                                   residual=w.residual)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end or len(times) >= 20:
+            break
+    t = statistics.median(times)
+    return t, len(times), out, inter
+
+
+def host_bits(torch, t):
+    import numpy as np
+    t = t.cpu()
+    if t.element_size() == 4:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py runs on one GPU only: the all-reduce core here is one GPU's share of the work "
+              f"(all rank partials in local HBM); --gpus {max(args.gpus, world)} is not supported.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tensor_all_reduce_ar_amd as ar
+    from tensor_all_reduce_ar_amd import inputs
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    name = args.workload or inputs.FUSED_BF16_R8_2048x8192
+    t0 = time.time()
+    w = inputs.make(name)
+    if w.op != "fused":
+        raise SystemExit("--workload must name a fused workload")
+    print(f"[bench] inputs for {name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    f = bench_fused(torch, ar, w, args, stream)
+    gbps = f["bytes"] / (f["ms_step"] * 1e-3) / 1e9
+    achieved = f["bytes"] / (f["k_mean"] * 1e-3) / 1e9
+    print(f"[bench] fused: {f['ms_step'] * 1e3:.1f} us/step, kernel {f['k_mean'] * 1e3:.1f} us "
+          f"({achieved:.0f} GB/s)", file=sys.stderr, flush=True)
+    gpu_out, gpu_inter = host_bits(torch, f["out"]), host_bits(torch, f["inter"])
+    del f["out"], f["inter"]
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(f["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": name, "op": "RESIDUAL_RMS_NORM", "ranks": w.ranks, "tokens": w.rows,
+            "hidden": w.hidden, "bias": w.bias is not None, "residual": w.residual is not None, "eps": w.eps,
+            "bytes_per_step": f["bytes"], "rotating_input_sets": f["nsets"], "seeds": w.seeds,
+            "distribution": "normal(mean, variance): partials N(0,1/R), residual N(0,1), weight N(1,0.1)",
+        },
+        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "kernel": FUSED_KERNEL, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(FUSED_KERNEL, name),
+            "kernel_us_mean": round(f["k_mean"] * 1e3, 2), "kernel_us_median": round(f["k_med"] * 1e3, 2),
+            "kernel_us_min": round(f["k_min"] * 1e3, 2), "algorithmic_bytes_per_launch": f["bytes"],
+        },
+    }
+
+    if not args.no_sum:
+        sw = inputs.make(inputs.SUM_BF16_R4_8192x8192)
+        s = bench_sum(torch, ar, sw, args, stream)
+        s_ach = s["bytes"] / (s["k_mean"] * 1e-3) / 1e9
+        result["standalone_sum"] = {
+            "workload": sw.name, "kernel": SUM_KERNEL, "bytes_per_call": s["bytes"],
+            "us_per_call": round(s["ms_step"] * 1e3, 2), "kernel_us_mean": round(s["k_mean"] * 1e3, 2),
+            "gbps": round(s["bytes"] / (s["ms_step"] * 1e-3) / 1e9, 1), "achieved": round(s_ach, 1),
+            "frac": round(s_ach / HBM_PEAK_GBPS, 4), "steps": s["steps"], "rotating_input_sets": s["nsets"],
+            "traffic": measured_traffic(SUM_KERNEL, sw.name),
+        }
+        print(f"[bench] sum: kernel {s['k_mean'] * 1e3:.1f} us ({s_ach:.0f} GB/s)", file=sys.stderr, flush=True)
+        del sw
+
+    result["copy_ceiling_gbps"] = round(copy_ceiling(torch, stream), 1)
+
+    if not args.no_cpu_baseline:
+        t, reps, ref_out, ref_inter = cpu_baseline(w, args.cpu_seconds)
+        sig_ok = np.array_equal(gpu_inter, ref_inter.view(gpu_inter.dtype))
+        o = lambda b: np.where(b.astype(np.int64) & 0x8000, 0x8000 - b.astype(np.int64), b.astype(np.int64))
+        ulp = int(np.abs(o(gpu_out) - o(ref_out.view(np.uint16))).max()) if w.dtype != "fp32" else None
+        result["cpu_baseline"] = {
+            "value": round(w.algorithmic_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole {name} call ({w.rows} rows), {reps} run(s), median {t:.2f} s",
+            "host_cpu": platform.processor() or platform.machine(), "host_logical_cpus": os.cpu_count(),
+            "gpu_vs_oracle": {"intermediate_bitexact": bool(sig_ok), "output_max_ulp": ulp},
+        }
+        print(f"[bench] oracle: {t:.2f} s per call", file=sys.stderr, flush=True)
+
+    result["versions"] = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                          "source_hash": source_hash()}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,6 +1,14 @@
 """MI355X (gfx950) all-reduce core: the rank-partial sum and the sum fused
-with bias, residual and RMSNorm, as hand-written HIP kernels behind a C ABI.
+with bias, residual and RMSNorm, as hand-written HIP kernels behind a C ABI
+(include/ar.h, built into libar.so).
 
-The binding (``ar``) loads ``libar.so`` on first use; importing this package
-does not touch the GPU.
+Importing this package does not touch the GPU; the library is loaded on the
+first call and its absence is an error.
 """
+from .ar import (AR_BF16, AR_FP16, AR_FP32, AR_FUSION_NONE, AR_FUSION_RESIDUAL_RMS_NORM, AR_MAX_RANKS, ArError,
+                 Params, ar_configuration_supported, ar_last_hip_error, ar_residual_rmsnorm, ar_status_string,
+                 ar_sum, ar_workspace_size, make_params)
+
+__all__ = ["ar_sum", "ar_residual_rmsnorm", "ar_configuration_supported", "ar_workspace_size", "ar_status_string",
+           "ar_last_hip_error", "Params", "make_params", "ArError", "AR_FP32", "AR_FP16", "AR_BF16",
+           "AR_FUSION_NONE", "AR_FUSION_RESIDUAL_RMS_NORM", "AR_MAX_RANKS"]

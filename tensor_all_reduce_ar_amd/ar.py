@@ -1,0 +1,198 @@
+"""ctypes binding of ``libar.so`` (C ABI in include/ar.h).
+
+Argument marshalling only: every step of both ops runs in the HIP kernels of
+csrc/ar.hip. torch supplies device memory and streams; tensors must be
+contiguous CUDA (HIP) tensors of one dtype. The library is loaded on first use
+and a missing library is an error (there is no fallback path).
+
+Entry points, same names as the C ABI:
+  ar_sum(partials, out)                                   fusion op NONE
+  ar_residual_rmsnorm(partials, weight, eps, out, intermediate,
+                      bias=None, residual=None, hidden_size=None)
+                                                          fusion op RESIDUAL_RMS_NORM
+  ar_configuration_supported(params, fusion_op), ar_workspace_size(params),
+  ar_status_string(code), ar_last_hip_error()
+plus ``Params`` / ``make_params`` and ``call`` for raw-pointer use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libar.so")
+
+AR_MAX_RANKS = 8
+AR_FP32, AR_FP16, AR_BF16 = 0, 1, 2
+AR_FUSION_NONE, AR_FUSION_RESIDUAL_RMS_NORM = 0, 1
+AR_OK = 0
+AR_ERR_NULL, AR_ERR_RANKS, AR_ERR_DTYPE, AR_ERR_SHAPE = -1, -2, -3, -4
+AR_ERR_EPS, AR_ERR_ALIAS, AR_ERR_ALIGN, AR_ERR_HIP = -5, -6, -7, -100
+
+# Every function include/ar.h declares.
+EXPORTS = ("ar_sum", "ar_residual_rmsnorm", "ar_configuration_supported", "ar_workspace_size",
+           "ar_status_string", "ar_last_hip_error")
+
+
+class FusionParams(ctypes.Structure):
+    """ar_fusion_params_t (mirrors "type.d2" AllReduceFusionParams)."""
+    _fields_ = [
+        ("bias_buffer", ctypes.c_void_p),
+        ("residual_buffer", ctypes.c_void_p),
+        ("hidden_size", ctypes.c_int32),
+        ("weight_buffer", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("intermediate_buffer", ctypes.c_void_p),
+    ]
+
+
+class Params(ctypes.Structure):
+    """ar_params_t (mirrors "type.d2" AllReduceParams)."""
+    _fields_ = [
+        ("elts_total", ctypes.c_size_t),
+        ("ranks", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("input_buffer_ptrs", ctypes.c_void_p * AR_MAX_RANKS),
+        ("local_output_buffer_ptr", ctypes.c_void_p),
+        ("fusion_params", FusionParams),
+    ]
+
+
+class ArError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = f"{what}: {ar_status_string(status)}"
+        if status == AR_ERR_HIP:
+            msg += f" (hipError_t {ar_last_hip_error()})"
+        super().__init__(msg)
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m tensor_all_reduce_ar_amd.build`")
+    L = ctypes.CDLL(path)
+    P = ctypes.POINTER(Params)
+    L.ar_sum.argtypes = [P, ctypes.c_void_p]
+    L.ar_sum.restype = ctypes.c_int32
+    L.ar_residual_rmsnorm.argtypes = [P, ctypes.c_void_p]
+    L.ar_residual_rmsnorm.restype = ctypes.c_int32
+    L.ar_configuration_supported.argtypes = [P, ctypes.c_int32]
+    L.ar_configuration_supported.restype = ctypes.c_int32
+    L.ar_workspace_size.argtypes = [P]
+    L.ar_workspace_size.restype = ctypes.c_size_t
+    L.ar_status_string.argtypes = [ctypes.c_int32]
+    L.ar_status_string.restype = ctypes.c_char_p
+    L.ar_last_hip_error.argtypes = []
+    L.ar_last_hip_error.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def ar_status_string(status: int) -> str:
+    return load().ar_status_string(status).decode()
+
+
+def ar_last_hip_error() -> int:
+    return load().ar_last_hip_error()
+
+
+def make_params(elts_total: int, ranks: int, dtype: int, inputs: Sequence[int], output: int,
+                hidden_size: int = 0, weight: int = 0, eps: float = 0.0, intermediate: int = 0,
+                bias: int = 0, residual: int = 0) -> Params:
+    """Fill an ar_params_t from raw device addresses (0 = NULL)."""
+    p = Params()
+    p.elts_total = elts_total
+    p.ranks = ranks
+    p.dtype = dtype
+    for r, ptr in enumerate(list(inputs)[:AR_MAX_RANKS]):
+        p.input_buffer_ptrs[r] = ptr or None
+    p.local_output_buffer_ptr = output or None
+    f = p.fusion_params
+    f.bias_buffer = bias or None
+    f.residual_buffer = residual or None
+    f.hidden_size = hidden_size
+    f.weight_buffer = weight or None
+    f.eps = eps
+    f.intermediate_buffer = intermediate or None
+    return p
+
+
+def call(fn: str, params: Params, stream: Optional[int] = None) -> int:
+    """Call ar_sum / ar_residual_rmsnorm with a filled Params; returns the status."""
+    return getattr(load(), fn)(ctypes.byref(params), ctypes.c_void_p(stream or 0))
+
+
+def ar_configuration_supported(params: Params, fusion_op: int) -> int:
+    return load().ar_configuration_supported(ctypes.byref(params), fusion_op)
+
+
+def ar_workspace_size(params: Optional[Params] = None) -> int:
+    return load().ar_workspace_size(ctypes.byref(params) if params is not None else None)
+
+
+# ------------------------------------------------------------ torch front end
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: AR_FP32, torch.float16: AR_FP16, torch.bfloat16: AR_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check(t, name: str, dtype, numel: int):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def ar_sum(partials: Sequence, out, stream=None) -> None:
+    """out = sum of the partials (fusion op NONE), on `stream` (default: torch's current)."""
+    if not 1 <= len(partials) <= AR_MAX_RANKS:
+        raise ValueError(f"need 1..{AR_MAX_RANKS} partials, got {len(partials)}")
+    n, dt = out.numel(), out.dtype
+    ptrs = [_check(p, f"partial {r}", dt, n) for r, p in enumerate(partials)]
+    params = make_params(n, len(partials), _dtype_code(out), ptrs, _check(out, "out", dt, n))
+    st = call("ar_sum", params, _stream_handle(stream))
+    if st != AR_OK:
+        raise ArError(st, "ar_sum")
+
+
+def ar_residual_rmsnorm(partials: Sequence, weight, eps: float, out, intermediate, bias=None, residual=None,
+                        hidden_size: Optional[int] = None, stream=None) -> None:
+    """Fusion op RESIDUAL_RMS_NORM: intermediate = ((sum + bias) + residual),
+    out = RMSNorm(intermediate) * weight over rows of hidden_size elements
+    (default: the weight's length)."""
+    if not 1 <= len(partials) <= AR_MAX_RANKS:
+        raise ValueError(f"need 1..{AR_MAX_RANKS} partials, got {len(partials)}")
+    n, dt = out.numel(), out.dtype
+    H = int(hidden_size if hidden_size is not None else weight.numel())
+    ptrs = [_check(p, f"partial {r}", dt, n) for r, p in enumerate(partials)]
+    params = make_params(
+        n, len(partials), _dtype_code(out), ptrs, _check(out, "out", dt, n), hidden_size=H,
+        weight=_check(weight, "weight", dt, H), eps=float(eps),
+        intermediate=_check(intermediate, "intermediate", dt, n),
+        bias=_check(bias, "bias", dt, H) if bias is not None else 0,
+        residual=_check(residual, "residual", dt, n) if residual is not None else 0)
+    st = call("ar_residual_rmsnorm", params, _stream_handle(stream))
+    if st != AR_OK:
+        raise ArError(st, "ar_residual_rmsnorm")

@@ -1,0 +1,865 @@
+// ar.hip - the all-reduce core for MI355X (gfx950): rank-partial sum, and the
+// sum fused with GEMM bias, residual and RMSNorm. C ABI declared in ar.h.
+//
+// What is computed follows "All Reduce Plugin" (class AllReducePlugin: a SUM
+// over tensor-parallel ranks of row-parallel-linear activations, passthrough
+// with one rank) and "type.d2" (AllReduceParams, AllReduceFusionParams, enum
+// AllReduceFusionOp). The host dispatch mirrors the chain of "allreduce.d2"
+// (customAllReduce -> configurationSupported, AllReduceDispatchType ->
+// AllReduceDispatchRanksPerNode -> standalone or fused launch), re-done for one
+// GPU: the R partials are local HBM buffers, so there are no peer buffers,
+// barriers or flags, and the per-GPU work is the local core of the one-shot
+// kernels (read R buffers, add, write).
+//
+// Design for CDNA4 (all of it HBM-bound; no matrix cores, the op is not a
+// contraction):
+//  * every lane moves 16-byte packs (global_load_dwordx4 / global_store_dwordx4),
+//    a wave touching 1 KiB contiguous per buffer - the 16-byte pack unions of
+//    "type.d2" PackedOn16Bytes, here plain 4 x u32 vectors, with a bf16 pack
+//    alongside the fp32 and fp16 ones;
+//  * the rank count is a template parameter, so the rank loop is unrolled and
+//    all R loads of a pack are in flight together;
+//  * accumulation is fp32 in rank order 0..R-1 starting from rank 0's value,
+//    one round-to-nearest-even per stored value (v_cvt_pk_bf16_f32 /
+//    v_cvt_pk_f16_f32); no multiply sits in the sum, so no contraction can
+//    change it, and fp32 denormals are kept (the kernels' default mode);
+//  * the fused op runs one workgroup per row with the row held in registers:
+//    S is stored as soon as it is formed, the sum of squares of the rounded S
+//    is reduced with cross-lane shuffles inside each 64-wide wave, then
+//    through LDS across waves with a single barrier, and the normed row is
+//    written from registers - each input is read once and each output written
+//    once.
+// Shapes the vector path does not cover (pointers not 16-byte aligned, rows
+// whose byte size is not a multiple of 16, rows wider than the register
+// budget) run element-wise kernels with the same arithmetic.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "ar.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPackBytes = 16;
+constexpr int kWave = 64;
+constexpr int kSumThreads = 256;        // workgroup size of the sum kernels
+#ifndef AR_SUM_UNROLL
+#define AR_SUM_UNROLL 2                 // packs per lane per step of the sum
+#endif
+#ifndef AR_NT_LOADS
+#define AR_NT_LOADS 1                   // non-temporal (streaming) loads/stores
+#endif
+#ifndef AR_FUSED_THREADS
+#define AR_FUSED_THREADS 256            // preferred workgroup size of the fused kernel
+#endif
+constexpr int kMaxPPT = 8;              // packs per lane a fused row may hold in registers
+constexpr int kFusedMaxThreads = 256;   // launch bound of the register-row kernel
+constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
+constexpr int kElemThreads = 256;       // element-wise kernels
+constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
+
+// ---------------------------------------------------------------- loads/stores
+__device__ __forceinline__ u32x4 ld16(const u32x4 *p)
+{
+#if AR_NT_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+__device__ __forceinline__ void st16(u32x4 *p, u32x4 v)
+{
+#if AR_NT_LOADS
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// ------------------------------------------------------------- element types
+// V elements per 16-byte pack; widen() is exact; narrow() rounds to nearest even.
+struct Fp32 {
+    static constexpr int V = 4;
+    static constexpr int kSize = 4;
+    __device__ static void widen(u32x4 p, float *f)
+    {
+        f[0] = __builtin_bit_cast(float, p.x);
+        f[1] = __builtin_bit_cast(float, p.y);
+        f[2] = __builtin_bit_cast(float, p.z);
+        f[3] = __builtin_bit_cast(float, p.w);
+    }
+    __device__ static u32x4 narrow(const float *f)
+    {
+        return u32x4{__builtin_bit_cast(uint32_t, f[0]), __builtin_bit_cast(uint32_t, f[1]),
+                     __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3])};
+    }
+    __device__ static float load1(const void *b, size_t i) { return static_cast<const float *>(b)[i]; }
+    // Rounds x to the type, stores it, and returns the stored value widened.
+    __device__ static float store1(void *b, size_t i, float x)
+    {
+        static_cast<float *>(b)[i] = x;
+        return x;
+    }
+};
+
+struct Fp16 {
+    static constexpr int V = 8;
+    static constexpr int kSize = 2;
+    __device__ static void widen2(uint32_t w, float *f)
+    {
+        f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+        f[0] = v.x;
+        f[1] = v.y;
+    }
+    __device__ static uint32_t narrow2(float a, float b)
+    {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+    }
+    __device__ static void widen(u32x4 p, float *f)
+    {
+        widen2(p.x, f);
+        widen2(p.y, f + 2);
+        widen2(p.z, f + 4);
+        widen2(p.w, f + 6);
+    }
+    __device__ static u32x4 narrow(const float *f)
+    {
+        return u32x4{narrow2(f[0], f[1]), narrow2(f[2], f[3]), narrow2(f[4], f[5]), narrow2(f[6], f[7])};
+    }
+    __device__ static float load1(const void *b, size_t i)
+    {
+        return static_cast<float>(static_cast<const _Float16 *>(b)[i]);
+    }
+    __device__ static float store1(void *b, size_t i, float x)
+    {
+        _Float16 h = static_cast<_Float16>(x);
+        static_cast<_Float16 *>(b)[i] = h;
+        return static_cast<float>(h);
+    }
+};
+
+struct Bf16 {
+    static constexpr int V = 8;
+    static constexpr int kSize = 2;
+    // bf16 is the upper half of an fp32: widening is a shift.
+    __device__ static void widen2(uint32_t w, float *f)
+    {
+        f[0] = __builtin_bit_cast(float, w << 16);
+        f[1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+    }
+    __device__ static uint32_t narrow2(float a, float b)
+    {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+    }
+    __device__ static void widen(u32x4 p, float *f)
+    {
+        widen2(p.x, f);
+        widen2(p.y, f + 2);
+        widen2(p.z, f + 4);
+        widen2(p.w, f + 6);
+    }
+    __device__ static u32x4 narrow(const float *f)
+    {
+        return u32x4{narrow2(f[0], f[1]), narrow2(f[2], f[3]), narrow2(f[4], f[5]), narrow2(f[6], f[7])};
+    }
+    __device__ static float load1(const void *b, size_t i)
+    {
+        uint32_t h = static_cast<const uint16_t *>(b)[i];
+        return __builtin_bit_cast(float, h << 16);
+    }
+    __device__ static float store1(void *b, size_t i, float x)
+    {
+        __bf16 h = static_cast<__bf16>(x);
+        static_cast<__bf16 *>(b)[i] = h;
+        return static_cast<float>(h);
+    }
+};
+
+// ------------------------------------------------------------------- kernels
+struct SumArgs {
+    const void *in[AR_MAX_RANKS];
+    void *out;
+    size_t n;       // elements
+    size_t npacks;  // n / V, for the vector kernel
+};
+
+// acc[k] = P0[k] + P1[k] + ... in rank order, for one pack of each rank.
+template <class E, int R>
+__device__ __forceinline__ void rank_sum_pack(const u32x4 (&v)[R], float *acc)
+{
+    E::widen(v[0], acc);
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+        float t[E::V];
+        E::widen(v[r], t);
+#pragma unroll
+        for (int k = 0; k < E::V; ++k)
+            acc[k] = acc[k] + t[k];
+    }
+}
+
+template <class E, int R>
+__device__ __forceinline__ float rank_sum_elem(const SumArgs &a, size_t i)
+{
+    float acc = E::load1(a.in[0], i);
+#pragma unroll
+    for (int r = 1; r < R; ++r)
+        acc = acc + E::load1(a.in[r], i);
+    return acc;
+}
+
+// Sum over 16-byte packs; every pointer 16-byte aligned. Each step a lane
+// loads U packs of each of the R ranks (all in flight), adds, and stores U
+// packs; the workgroup covers kSumThreads*U consecutive packs, coalesced.
+// The packs after the last full step, and the n % V elements after the last
+// pack, are done by the last workgroup.
+template <class E, int R, int U>
+__global__ __launch_bounds__(kSumThreads) void ar_sum_pack_kernel(SumArgs a)
+{
+    const u32x4 *in[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        in[r] = static_cast<const u32x4 *>(a.in[r]);
+    u32x4 *out = static_cast<u32x4 *>(a.out);
+
+    const size_t step = static_cast<size_t>(kSumThreads) * U;
+    const size_t nfull = a.npacks / step;
+    for (size_t c = blockIdx.x; c < nfull; c += gridDim.x) {
+        const size_t base = c * step + threadIdx.x;
+        u32x4 v[U][R];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                v[u][r] = ld16(in[r] + base + static_cast<size_t>(u) * kSumThreads);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float acc[E::V];
+            rank_sum_pack<E, R>(v[u], acc);
+            st16(out + base + static_cast<size_t>(u) * kSumThreads, E::narrow(acc));
+        }
+    }
+
+    if (blockIdx.x == gridDim.x - 1) {
+        for (size_t j = nfull * step + threadIdx.x; j < a.npacks; j += kSumThreads) {
+            u32x4 v[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                v[r] = ld16(in[r] + j);
+            float acc[E::V];
+            rank_sum_pack<E, R>(v, acc);
+            st16(out + j, E::narrow(acc));
+        }
+        const size_t i = a.npacks * E::V + threadIdx.x;
+        if (i < a.n)
+            E::store1(a.out, i, rank_sum_elem<E, R>(a, i));
+    }
+}
+
+// Element-wise sum for pointers that are only element-aligned.
+template <class E, int R>
+__global__ __launch_bounds__(kElemThreads) void ar_sum_elem_kernel(SumArgs a)
+{
+    const size_t stride = static_cast<size_t>(gridDim.x) * kElemThreads;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * kElemThreads + threadIdx.x; i < a.n; i += stride)
+        E::store1(a.out, i, rank_sum_elem<E, R>(a, i));
+}
+
+struct FusedArgs {
+    const void *in[AR_MAX_RANKS];
+    const void *bias;      // [H] or NULL
+    const void *residual;  // [rows, H] or NULL
+    const void *weight;    // [H]
+    void *out;             // [rows, H]
+    void *inter;           // [rows, H]
+    size_t rows;
+    int hidden;            // H
+    int ppr;               // packs per row (vector kernel)
+    float eps;
+};
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// Sum of x over the workgroup, the same value in every lane. Fixed order
+// (lanes by xor-butterfly, then waves 0..n-1), so repeat calls agree bitwise.
+// One barrier; `part` must not be reused before the next barrier.
+__device__ __forceinline__ float block_sum(float x, float *part)
+{
+    x = wave_sum(x);
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    if (lane == 0)
+        part[wave] = x;
+    __syncthreads();
+    float t = part[0];
+    const int nw = blockDim.x / kWave;
+    for (int w = 1; w < nw; ++w)
+        t = t + part[w];
+    return t;
+}
+
+// rstd = 1 / sqrt(mean square + eps), correctly rounded division and root.
+__device__ __forceinline__ float rms_scale(float ss, int hidden, float eps)
+{
+    return 1.0f / __builtin_sqrtf(ss / static_cast<float>(hidden) + eps);
+}
+
+// S pack = T( ((P0 + ... + P(R-1)) + bias) + residual ), fp32 inside.
+template <class E, int R>
+__device__ __forceinline__ u32x4 fused_pre_norm(const u32x4 (&v)[R], bool has_bias, u32x4 bq, bool has_res, u32x4 rq)
+{
+    float acc[E::V];
+    rank_sum_pack<E, R>(v, acc);
+    if (has_bias) {
+        float t[E::V];
+        E::widen(bq, t);
+#pragma unroll
+        for (int k = 0; k < E::V; ++k)
+            acc[k] = acc[k] + t[k];
+    }
+    if (has_res) {
+        float t[E::V];
+        E::widen(rq, t);
+#pragma unroll
+        for (int k = 0; k < E::V; ++k)
+            acc[k] = acc[k] + t[k];
+    }
+    return E::narrow(acc);
+}
+
+// Sum of squares of the (rounded) S values of one pack, in element order.
+template <class E>
+__device__ __forceinline__ float sum_squares(u32x4 sp)
+{
+    float s[E::V];
+    E::widen(sp, s);
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < E::V; ++k)
+        ss += s[k] * s[k];
+    return ss;
+}
+
+// Output pack = T( S * rstd * weight ).
+template <class E>
+__device__ __forceinline__ u32x4 normed_pack(u32x4 sp, float rstd, u32x4 wp)
+{
+    float s[E::V], w[E::V], o[E::V];
+    E::widen(sp, s);
+    E::widen(wp, w);
+#pragma unroll
+    for (int k = 0; k < E::V; ++k)
+        o[k] = s[k] * rstd * w[k];
+    return E::narrow(o);
+}
+
+// Fused op, one row per workgroup (rows beyond the grid loop), for rows of
+// up to kMaxPPT * kFusedMaxThreads packs. Lane l holds packs l, l+T, ...,
+// l+(PPT-1)T of the row (T = workgroup size), so each load instruction of a
+// wave covers 1 KiB contiguous. The rounded S stays in registers as packs
+// (4 VGPRs per pack) and the weight packs are loaded before the barrier.
+template <class E, int R, int PPT>
+__global__ __launch_bounds__(kFusedMaxThreads) void ar_rmsnorm_pack_kernel(FusedArgs a)
+{
+    __shared__ float part[kFusedMaxThreads / kWave];
+    const u32x4 *bias = static_cast<const u32x4 *>(a.bias);
+    const u32x4 *weight = static_cast<const u32x4 *>(a.weight);
+    const int T = blockDim.x;
+
+    for (size_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const size_t row0 = row * static_cast<size_t>(a.ppr);
+        u32x4 sp[PPT], w[PPT];
+        float ss = 0.0f;
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int j = threadIdx.x + p * T;
+            if (j < a.ppr) {
+                u32x4 v[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    v[r] = ld16(static_cast<const u32x4 *>(a.in[r]) + row0 + j);
+                u32x4 bq = {0, 0, 0, 0}, rq = {0, 0, 0, 0};
+                if (bias)
+                    bq = bias[j];
+                if (a.residual)
+                    rq = ld16(static_cast<const u32x4 *>(a.residual) + row0 + j);
+                w[p] = weight[j];
+                sp[p] = fused_pre_norm<E, R>(v, bias != nullptr, bq, a.residual != nullptr, rq);
+                st16(static_cast<u32x4 *>(a.inter) + row0 + j, sp[p]);
+                ss += sum_squares<E>(sp[p]);
+            }
+        }
+
+        const float rstd = rms_scale(block_sum(ss, part), a.hidden, a.eps);
+
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int j = threadIdx.x + p * T;
+            if (j < a.ppr)
+                st16(static_cast<u32x4 *>(a.out) + row0 + j, normed_pack<E>(sp[p], rstd, w[p]));
+        }
+        __syncthreads();  // `part` is rewritten by the next row
+    }
+}
+
+// Fused op for rows wider than the register path, still 16-byte packs: pass
+// 1 forms, stores and squares S; pass 2 re-reads the S packs this lane stored
+// (normal stores, so they are likely still in L2) and writes the norm.
+template <class E, int R>
+__global__ __launch_bounds__(kWideThreads) void ar_rmsnorm_wide_kernel(FusedArgs a)
+{
+    __shared__ float part[kWideThreads / kWave];
+    const u32x4 *bias = static_cast<const u32x4 *>(a.bias);
+    const u32x4 *weight = static_cast<const u32x4 *>(a.weight);
+
+    for (size_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const size_t row0 = row * static_cast<size_t>(a.ppr);
+        u32x4 *inter = static_cast<u32x4 *>(a.inter) + row0;
+        float ss = 0.0f;
+        for (int j = threadIdx.x; j < a.ppr; j += kWideThreads) {
+            u32x4 v[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                v[r] = ld16(static_cast<const u32x4 *>(a.in[r]) + row0 + j);
+            u32x4 bq = {0, 0, 0, 0}, rq = {0, 0, 0, 0};
+            if (bias)
+                bq = bias[j];
+            if (a.residual)
+                rq = ld16(static_cast<const u32x4 *>(a.residual) + row0 + j);
+            const u32x4 sp = fused_pre_norm<E, R>(v, bias != nullptr, bq, a.residual != nullptr, rq);
+            inter[j] = sp;
+            ss += sum_squares<E>(sp);
+        }
+        const float rstd = rms_scale(block_sum(ss, part), a.hidden, a.eps);
+        for (int j = threadIdx.x; j < a.ppr; j += kWideThreads)
+            st16(static_cast<u32x4 *>(a.out) + row0 + j, normed_pack<E>(inter[j], rstd, weight[j]));
+        __syncthreads();
+    }
+}
+
+// Fused op, element-wise, one row per workgroup: pass 1 forms, stores and
+// squares S; pass 2 re-reads the S this lane stored and writes the norm.
+template <class E, int R>
+__global__ __launch_bounds__(kElemThreads) void ar_rmsnorm_elem_kernel(FusedArgs a)
+{
+    __shared__ float part[kElemThreads / kWave];
+    SumArgs sa;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        sa.in[r] = a.in[r];
+    const size_t H = static_cast<size_t>(a.hidden);
+
+    for (size_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const size_t row0 = row * H;
+        float ss = 0.0f;
+        for (size_t h = threadIdx.x; h < H; h += kElemThreads) {
+            float acc = rank_sum_elem<E, R>(sa, row0 + h);
+            if (a.bias)
+                acc = acc + E::load1(a.bias, h);
+            if (a.residual)
+                acc = acc + E::load1(a.residual, row0 + h);
+            const float s = E::store1(a.inter, row0 + h, acc);
+            ss += s * s;
+        }
+        const float rstd = rms_scale(block_sum(ss, part), a.hidden, a.eps);
+        for (size_t h = threadIdx.x; h < H; h += kElemThreads) {
+            const float s = E::load1(a.inter, row0 + h);
+            E::store1(a.out, row0 + h, s * rstd * E::load1(a.weight, h));
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------ host dispatch
+thread_local int32_t g_last_hip_error = 0;
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *e = getenv("AR_LOG");
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
+}
+
+size_t elem_size(int32_t dtype) { return dtype == AR_FP32 ? 4 : 2; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [p, p+n) and [q, q+m) share a byte.
+bool overlap(const void *p, size_t n, const void *q, size_t m)
+{
+    if (!p || !q || !n || !m)
+        return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + m && b < a + n;
+}
+
+// An output may coincide exactly with a full-size input, not overlap it partly.
+bool bad_alias(const void *out, const void *in, size_t bytes)
+{
+    return in != out && overlap(out, bytes, in, bytes);
+}
+
+int32_t validate_common(const ar_params_t *p)
+{
+    if (!p)
+        return AR_ERR_NULL;
+    if (p->dtype != AR_FP32 && p->dtype != AR_FP16 && p->dtype != AR_BF16)
+        return AR_ERR_DTYPE;
+    if (p->ranks < 1 || p->ranks > AR_MAX_RANKS)
+        return AR_ERR_RANKS;
+    return AR_OK;
+}
+
+int32_t validate_sum(const ar_params_t *p)
+{
+    int32_t st = validate_common(p);
+    if (st != AR_OK || p->elts_total == 0)
+        return st;
+    const size_t s = elem_size(p->dtype), bytes = p->elts_total * s;
+    if (!p->local_output_buffer_ptr)
+        return AR_ERR_NULL;
+    for (int r = 0; r < p->ranks; ++r)
+        if (!p->input_buffer_ptrs[r])
+            return AR_ERR_NULL;
+    if (!aligned(p->local_output_buffer_ptr, s))
+        return AR_ERR_ALIGN;
+    for (int r = 0; r < p->ranks; ++r)
+        if (!aligned(p->input_buffer_ptrs[r], s))
+            return AR_ERR_ALIGN;
+    for (int r = 0; r < p->ranks; ++r)
+        if (bad_alias(p->local_output_buffer_ptr, p->input_buffer_ptrs[r], bytes))
+            return AR_ERR_ALIAS;
+    return AR_OK;
+}
+
+int32_t validate_fused(const ar_params_t *p)
+{
+    int32_t st = validate_common(p);
+    if (st != AR_OK)
+        return st;
+    const ar_fusion_params_t &f = p->fusion_params;
+    if (f.hidden_size <= 0 || p->elts_total % static_cast<size_t>(f.hidden_size) != 0)
+        return AR_ERR_SHAPE;
+    if (!(f.eps >= 0.0f) || isinf(f.eps))
+        return AR_ERR_EPS;
+    if (p->elts_total == 0)
+        return AR_OK;
+    const size_t s = elem_size(p->dtype), bytes = p->elts_total * s;
+    const size_t hbytes = static_cast<size_t>(f.hidden_size) * s;
+    void *out = p->local_output_buffer_ptr, *inter = f.intermediate_buffer;
+    if (!out || !inter || !f.weight_buffer)
+        return AR_ERR_NULL;
+    for (int r = 0; r < p->ranks; ++r)
+        if (!p->input_buffer_ptrs[r])
+            return AR_ERR_NULL;
+    const void *ptrs[] = {out, inter, f.weight_buffer, f.bias_buffer, f.residual_buffer};
+    for (const void *q : ptrs)
+        if (q && !aligned(q, s))
+            return AR_ERR_ALIGN;
+    for (int r = 0; r < p->ranks; ++r)
+        if (!aligned(p->input_buffer_ptrs[r], s))
+            return AR_ERR_ALIGN;
+    if (overlap(out, bytes, inter, bytes))
+        return AR_ERR_ALIAS;
+    for (void *o : {out, inter}) {
+        for (int r = 0; r < p->ranks; ++r)
+            if (bad_alias(o, p->input_buffer_ptrs[r], bytes))
+                return AR_ERR_ALIAS;
+        if (overlap(o, bytes, f.weight_buffer, hbytes) || overlap(o, bytes, f.bias_buffer, hbytes))
+            return AR_ERR_ALIAS;
+    }
+    if (bad_alias(inter, f.residual_buffer, bytes) || bad_alias(out, f.residual_buffer, bytes))
+        return AR_ERR_ALIAS;
+    return AR_OK;
+}
+
+bool sum_vector_ok(const ar_params_t *p)
+{
+    if (!aligned(p->local_output_buffer_ptr, kPackBytes))
+        return false;
+    for (int r = 0; r < p->ranks; ++r)
+        if (!aligned(p->input_buffer_ptrs[r], kPackBytes))
+            return false;
+    return true;
+}
+
+// Packs per lane and workgroup size of the register-row kernel for a row of
+// `ppr` packs: PPT = ceil(ppr / AR_FUSED_THREADS) (at most kMaxPPT), then the
+// fewest whole waves that cover the row. Returns false (PPT = 0) when the row
+// needs more than kMaxPPT * kFusedMaxThreads packs: the wide kernel takes it.
+bool fused_geometry(int ppr, int *ppt, int *threads)
+{
+    static_assert(AR_FUSED_THREADS >= kWave && AR_FUSED_THREADS <= kFusedMaxThreads, "fused workgroup size");
+    int k = (ppr + AR_FUSED_THREADS - 1) / AR_FUSED_THREADS;
+    if (k < 1)
+        k = 1;
+    if (k > kMaxPPT)
+        k = kMaxPPT;
+    int t = (ppr + k - 1) / k;
+    t = (t + kWave - 1) / kWave * kWave;
+    if (t > kFusedMaxThreads) {
+        *ppt = 0;
+        *threads = kWideThreads;
+        return false;
+    }
+    *ppt = k;
+    *threads = t;
+    return true;
+}
+
+bool fused_vector_ok(const ar_params_t *p, int *ppt, int *threads)
+{
+    const ar_fusion_params_t &f = p->fusion_params;
+    const size_t s = elem_size(p->dtype);
+    if ((static_cast<size_t>(f.hidden_size) * s) % kPackBytes != 0)
+        return false;
+    const void *ptrs[] = {p->local_output_buffer_ptr, f.intermediate_buffer, f.weight_buffer, f.bias_buffer,
+                          f.residual_buffer};
+    for (const void *q : ptrs)
+        if (q && !aligned(q, kPackBytes))
+            return false;
+    for (int r = 0; r < p->ranks; ++r)
+        if (!aligned(p->input_buffer_ptrs[r], kPackBytes))
+            return false;
+    const size_t ppr = static_cast<size_t>(f.hidden_size) * s / kPackBytes;
+    fused_geometry(static_cast<int>(ppr), ppt, threads);
+    return true;
+}
+
+int32_t check_launch(const char *what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int32_t>(e);
+        if (log_enabled())
+            fprintf(stderr, "[ar] %s: %s\n", what, hipGetErrorString(e));
+        return AR_ERR_HIP;
+    }
+    return AR_OK;
+}
+
+unsigned clamp_grid(size_t blocks)
+{
+    if (blocks < 1)
+        return 1;
+    return blocks > kMaxGrid ? kMaxGrid : static_cast<unsigned>(blocks);
+}
+
+template <class E, int R>
+int32_t launch_sum(const ar_params_t *p, hipStream_t stream, bool vec)
+{
+    SumArgs a = {};
+    for (int r = 0; r < R; ++r)
+        a.in[r] = p->input_buffer_ptrs[r];
+    a.out = p->local_output_buffer_ptr;
+    a.n = p->elts_total;
+    if (vec) {
+        a.npacks = a.n / E::V;
+        const size_t step = static_cast<size_t>(kSumThreads) * AR_SUM_UNROLL;
+        const unsigned grid = clamp_grid(a.npacks / step);
+        if (log_enabled())
+            fprintf(stderr, "[ar] sum pack R=%d V=%d n=%zu grid=%u block=%d unroll=%d\n", R, E::V, a.n, grid,
+                    kSumThreads, AR_SUM_UNROLL);
+        hipLaunchKernelGGL((ar_sum_pack_kernel<E, R, AR_SUM_UNROLL>), dim3(grid), dim3(kSumThreads), 0, stream, a);
+    } else {
+        const unsigned grid = clamp_grid((a.n + kElemThreads - 1) / kElemThreads);
+        if (log_enabled())
+            fprintf(stderr, "[ar] sum elem R=%d n=%zu grid=%u\n", R, a.n, grid);
+        hipLaunchKernelGGL((ar_sum_elem_kernel<E, R>), dim3(grid), dim3(kElemThreads), 0, stream, a);
+    }
+    return check_launch("ar_sum launch");
+}
+
+template <class E, int R, int PPT>
+void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, hipStream_t stream)
+{
+    hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT>), dim3(grid), dim3(threads), 0, stream, a);
+}
+
+template <class E, int R>
+int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec, int ppt, int threads)
+{
+    const ar_fusion_params_t &f = p->fusion_params;
+    FusedArgs a = {};
+    for (int r = 0; r < R; ++r)
+        a.in[r] = p->input_buffer_ptrs[r];
+    a.bias = f.bias_buffer;
+    a.residual = f.residual_buffer;
+    a.weight = f.weight_buffer;
+    a.out = p->local_output_buffer_ptr;
+    a.inter = f.intermediate_buffer;
+    a.hidden = f.hidden_size;
+    a.rows = p->elts_total / static_cast<size_t>(f.hidden_size);
+    a.eps = f.eps;
+    const unsigned grid = clamp_grid(a.rows);
+    if (vec && ppt == 0) {
+        a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
+        if (log_enabled())
+            fprintf(stderr, "[ar] fused wide R=%d rows=%zu H=%d ppr=%d block=%d grid=%u\n", R, a.rows, a.hidden,
+                    a.ppr, kWideThreads, grid);
+        hipLaunchKernelGGL((ar_rmsnorm_wide_kernel<E, R>), dim3(grid), dim3(kWideThreads), 0, stream, a);
+    } else if (vec) {
+        a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
+        if (log_enabled())
+            fprintf(stderr, "[ar] fused pack R=%d rows=%zu H=%d ppr=%d ppt=%d block=%d grid=%u\n", R, a.rows,
+                    a.hidden, a.ppr, ppt, threads, grid);
+        switch (ppt) {
+        case 1: launch_fused_pack<E, R, 1>(a, grid, threads, stream); break;
+        case 2: launch_fused_pack<E, R, 2>(a, grid, threads, stream); break;
+        case 3: launch_fused_pack<E, R, 3>(a, grid, threads, stream); break;
+        case 4: launch_fused_pack<E, R, 4>(a, grid, threads, stream); break;
+        case 5: launch_fused_pack<E, R, 5>(a, grid, threads, stream); break;
+        case 6: launch_fused_pack<E, R, 6>(a, grid, threads, stream); break;
+        case 7: launch_fused_pack<E, R, 7>(a, grid, threads, stream); break;
+        case 8: launch_fused_pack<E, R, 8>(a, grid, threads, stream); break;
+        default: return AR_ERR_SHAPE;  // unreachable: fused_geometry yields 0..kMaxPPT
+        }
+    } else {
+        if (log_enabled())
+            fprintf(stderr, "[ar] fused elem R=%d rows=%zu H=%d grid=%u\n", R, a.rows, a.hidden, grid);
+        hipLaunchKernelGGL((ar_rmsnorm_elem_kernel<E, R>), dim3(grid), dim3(kElemThreads), 0, stream, a);
+    }
+    return check_launch("ar_residual_rmsnorm launch");
+}
+
+// AllReduceDispatchType -> AllReduceDispatchRanksPerNode, as template
+// parameters: the element type, then the rank count.
+template <template <class, int> class Launcher, class... Args>
+int32_t dispatch(int32_t dtype, int ranks, Args... args)
+{
+    switch (dtype) {
+    case AR_FP32: return Launcher<Fp32, 0>::by_ranks(ranks, args...);
+    case AR_FP16: return Launcher<Fp16, 0>::by_ranks(ranks, args...);
+    default: return Launcher<Bf16, 0>::by_ranks(ranks, args...);
+    }
+}
+
+#define AR_BY_RANKS(call)                        \
+    switch (ranks) {                             \
+    case 1: return call(1);                      \
+    case 2: return call(2);                      \
+    case 3: return call(3);                      \
+    case 4: return call(4);                      \
+    case 5: return call(5);                      \
+    case 6: return call(6);                      \
+    case 7: return call(7);                      \
+    default: return call(8);                     \
+    }
+
+template <class E, int Unused>
+struct SumLauncher {
+    static int32_t by_ranks(int ranks, const ar_params_t *p, hipStream_t s, bool vec)
+    {
+#define AR_CALL(R) launch_sum<E, R>(p, s, vec)
+        AR_BY_RANKS(AR_CALL)
+#undef AR_CALL
+    }
+};
+
+template <class E, int Unused>
+struct FusedLauncher {
+    static int32_t by_ranks(int ranks, const ar_params_t *p, hipStream_t s, bool vec, int ppt, int threads)
+    {
+#define AR_CALL(R) launch_fused<E, R>(p, s, vec, ppt, threads)
+        AR_BY_RANKS(AR_CALL)
+#undef AR_CALL
+    }
+};
+
+}  // namespace
+
+// ------------------------------------------------------------------- C ABI
+extern "C" {
+
+int32_t ar_sum(const ar_params_t *p, void *hip_stream)
+{
+    int32_t st = validate_sum(p);
+    if (st != AR_OK || p->elts_total == 0)
+        return st;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (p->ranks == 1) {  // passthrough
+        if (p->local_output_buffer_ptr == p->input_buffer_ptrs[0])
+            return AR_OK;
+        hipError_t e = hipMemcpyAsync(p->local_output_buffer_ptr, p->input_buffer_ptrs[0],
+                                      p->elts_total * elem_size(p->dtype), hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) {
+            g_last_hip_error = static_cast<int32_t>(e);
+            return AR_ERR_HIP;
+        }
+        return AR_OK;
+    }
+    return dispatch<SumLauncher>(p->dtype, p->ranks, p, stream, sum_vector_ok(p));
+}
+
+int32_t ar_residual_rmsnorm(const ar_params_t *p, void *hip_stream)
+{
+    int32_t st = validate_fused(p);
+    if (st != AR_OK || p->elts_total == 0)
+        return st;
+    int ppt = 0, threads = 0;
+    const bool vec = fused_vector_ok(p, &ppt, &threads);
+    return dispatch<FusedLauncher>(p->dtype, p->ranks, p, static_cast<hipStream_t>(hip_stream), vec, ppt, threads);
+}
+
+int32_t ar_configuration_supported(const ar_params_t *p, int32_t fusion_op)
+{
+    if (fusion_op == AR_FUSION_NONE) {
+        int32_t st = validate_sum(p);
+        if (st != AR_OK)
+            return st;
+        return (p->elts_total == 0 || p->ranks == 1 || sum_vector_ok(p)) ? 1 : 0;
+    }
+    if (fusion_op == AR_FUSION_RESIDUAL_RMS_NORM) {
+        int32_t st = validate_fused(p);
+        if (st != AR_OK)
+            return st;
+        if (p->elts_total == 0)
+            return 1;
+        int ppt = 0, threads = 0;
+        return fused_vector_ok(p, &ppt, &threads) ? 1 : 0;
+    }
+    return AR_ERR_SHAPE;
+}
+
+size_t ar_workspace_size(const ar_params_t *p)
+{
+    (void)p;
+    return 0;
+}
+
+const char *ar_status_string(int32_t status)
+{
+    switch (status) {
+    case AR_OK: return "AR_OK: success";
+    case AR_ERR_NULL: return "AR_ERR_NULL: a required pointer is NULL";
+    case AR_ERR_RANKS: return "AR_ERR_RANKS: ranks outside 1..AR_MAX_RANKS";
+    case AR_ERR_DTYPE: return "AR_ERR_DTYPE: unknown element type";
+    case AR_ERR_SHAPE: return "AR_ERR_SHAPE: hidden_size <= 0 or elts_total not a multiple of it (or unknown fusion op)";
+    case AR_ERR_EPS: return "AR_ERR_EPS: eps is NaN, infinite or negative";
+    case AR_ERR_ALIAS: return "AR_ERR_ALIAS: an output partly overlaps an input or the other output";
+    case AR_ERR_ALIGN: return "AR_ERR_ALIGN: a buffer is not aligned to the element size";
+    case AR_ERR_HIP: return "AR_ERR_HIP: a HIP call failed (see ar_last_hip_error)";
+    default: return "unknown ar status";
+    }
+}
+
+int32_t ar_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,289 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Rules: sums and the pre-norm sum S are compared bit for bit (same fp32 adds
+in the same rank order, one rounding); the normed output is within 1e-5
+relative for fp32 and within 2 ulp for fp16/bf16. Every output buffer has
+canary guard bands that must come back untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_all_reduce_ar_amd as ar
+from tensor_all_reduce_ar_amd import inputs
+from tensor_all_reduce_ar_amd.ar import call, make_params
+
+from gpu_util import (TORCH_DT, Guarded, assert_bitexact, assert_output_close, bits, dev, empty_host, host_bits,
+                      max_ulp, note)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DTYPES = ("fp32", "fp16", "bf16")
+CODE = {"fp32": ar.AR_FP32, "fp16": ar.AR_FP16, "bf16": ar.AR_BF16}
+
+
+def run_sum(w: inputs.Workload, offsets=None, out_offset=0):
+    """Run ar_sum on the workload; partial r may start `offsets[r]` elements
+    into its device buffer (to make pointers unaligned)."""
+    offsets = offsets or [0] * w.ranks
+    bufs = []
+    for p, off in zip(w.partials, offsets):
+        t = torch.empty(w.n + off, dtype=TORCH_DT[w.dtype], device="cuda")
+        t[off:].copy_(dev(p, w.dtype))
+        bufs.append(t[off:])
+    out = Guarded(w.n, w.dtype, out_offset)
+    ar.ar_sum(bufs, out.t)
+    torch.cuda.synchronize()
+    out.check_guards()
+    return host_bits(out.t)
+
+
+def ref_sum(w: inputs.Workload):
+    ref = empty_host(w.n, w.dtype)
+    oracle.ar_sum(w.dtype, w.partials, ref)
+    return bits(ref)
+
+
+def run_fused(w: inputs.Workload, stream=None):
+    parts = [dev(p, w.dtype) for p in w.partials]
+    out, inter = Guarded(w.n, w.dtype), Guarded(w.n, w.dtype)
+    ar.ar_residual_rmsnorm(parts, dev(w.weight, w.dtype), w.eps, out.t, inter.t,
+                           bias=dev(w.bias, w.dtype) if w.bias is not None else None,
+                           residual=dev(w.residual, w.dtype) if w.residual is not None else None,
+                           hidden_size=w.hidden, stream=stream)
+    torch.cuda.synchronize()
+    out.check_guards()
+    inter.check_guards()
+    return host_bits(out.t), host_bits(inter.t)
+
+
+def ref_fused(w: inputs.Workload):
+    out, inter = empty_host(w.n, w.dtype), empty_host(w.n, w.dtype)
+    oracle.ar_residual_rmsnorm(w.dtype, w.partials, w.hidden, w.weight, w.eps, out, inter, bias=w.bias,
+                               residual=w.residual)
+    return bits(out), bits(inter)
+
+
+def check_fused(w, got_out, got_inter):
+    ref_out, ref_inter = ref_fused(w)
+    assert_bitexact(got_inter, ref_inter, w.dtype, f"{w.name} intermediate")
+    assert_output_close(got_out, ref_out, w.dtype, f"{w.name} output")
+    return ref_out
+
+
+# ---------------------------------------------------- the named workloads
+@pytest.mark.parametrize("name", inputs.workload_names())
+def test_named_workload_matches_oracle(name):
+    note(f"[parity] workload {name}")
+    w = inputs.make(name)
+    if w.op == "sum":
+        assert_bitexact(run_sum(w), ref_sum(w), w.dtype, name)
+    else:
+        got_out, got_inter = run_fused(w)
+        ref_out = check_fused(w, got_out, got_inter)
+        if w.dtype != "fp32":
+            note(f"[parity] {name}: output max {max_ulp(got_out, ref_out, w.dtype)} ulp from the oracle")
+
+
+def test_golden_small_workloads():
+    """The small workloads also match the oracle's stored digests."""
+    import hashlib
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "oracle_small.json")) as f:
+        gold = json.load(f)
+    w = inputs.make(inputs.SUM_FP32_R2_4x256)
+    got = run_sum(w)
+    assert hashlib.sha256(got.tobytes()).hexdigest() == gold["workloads"][w.name]["out_sha256"]
+    for name in (inputs.FUSED_FP16_R8_16x4096, inputs.fused_fp16_r2_5120_name(7)):
+        w = inputs.make(name)
+        _, inter = run_fused(w)
+        assert hashlib.sha256(inter.tobytes()).hexdigest() == gold["workloads"][name]["intermediate_sha256"]
+
+
+# ------------------------------------------------------------------ sums
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ranks", range(1, 9))
+def test_sum_sizes_and_tails(dtype, ranks):
+    for n in (1, 7, 8, 9, 17, 1027, 2 * 256 * 8 + 5, 70001):
+        note(f"[parity] sum {dtype} R={ranks} n={n}")
+        w = inputs.random_sum(dtype, ranks, n, 1000 + 10 * ranks + n % 97)
+        assert_bitexact(run_sum(w), ref_sum(w), dtype, f"sum {dtype} R={ranks} n={n}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_sum_unaligned_pointers(dtype):
+    """Element-aligned but not 16-byte aligned buffers take the element-wise kernel."""
+    for offs, oo in (([1, 0, 0], 0), ([0, 0, 0], 1), ([3, 1, 2], 3)):
+        note(f"[parity] sum unaligned {dtype} offsets={offs} out={oo}")
+        w = inputs.random_sum(dtype, 3, 4099, 77)
+        assert_bitexact(run_sum(w, offs, oo), ref_sum(w), dtype, f"unaligned {offs}/{oo}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_sum_in_place(dtype):
+    w = inputs.random_sum(dtype, 4, 100003, 5)
+    parts = [dev(p, dtype) for p in w.partials]
+    ar.ar_sum(parts, parts[2])  # output is partial 2
+    torch.cuda.synchronize()
+    assert_bitexact(host_bits(parts[2]), ref_sum(w), dtype, "in place")
+    one = dev(w.partials[0], dtype)
+    ar.ar_sum([one], one)  # one rank, in place: nothing to do
+    torch.cuda.synchronize()
+    assert_bitexact(host_bits(one), bits(w.partials[0]), dtype, "passthrough in place")
+
+
+def test_sum_special_values_fp32():
+    s = 2.0 ** -149
+    p0 = np.array([np.inf, np.inf, np.nan, 1.0, -0.0, -0.0, s, 3 * s, 1.0, 2.0 ** -24] * 7, np.float32)
+    p1 = np.array([-np.inf, 1.0, 1.0, np.nan, -0.0, 0.0, s, -s, 2.0 ** -24, 2.0 ** -24] * 7, np.float32)
+    p2 = np.array([0.0, 0.0, 0.0, 0.0, -0.0, -0.0, s, 0.0, 2.0 ** -24, 1.0] * 7, np.float32)
+    w = inputs.Workload("special", "sum", "fp32", 3, p0.size, p0.size, [p0, p1, p2])
+    assert_bitexact(run_sum(w), ref_sum(w), "fp32", "special values")
+    assert_bitexact(run_sum(w, [1, 2, 3]), ref_sum(w), "fp32", "special values, element path")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_sum_rounding_edges(dtype):
+    """Overflow to Inf (fp16: 65504 + 16), ties to even, and values the
+    one-rounding rule decides, through both kernels."""
+    big = 65504.0 if dtype == "fp16" else 3.3895314e38
+    vals0 = [big, big, 1.0, 1.0, -1.0, 1.0, 0.5, -0.0] * 5
+    vals1 = [16.0, 15.0, 2.0 ** -11, 3 * 2.0 ** -11, -2.0 ** -8, 2.0 ** -9, 2.0 ** -12, -0.0] * 5
+    if dtype == "bf16":
+        vals1[:2] = [big / 2, 2.0 ** 100] * 1
+    p0 = inputs.to_dtype(np.array(vals0, np.float32), dtype)
+    p1 = inputs.to_dtype(np.array(vals1, np.float32), dtype)
+    p2 = inputs.to_dtype(np.array([0.0, 0.0, 0.0, 0.0, 0.0, 2.0 ** -9, 0.0, -0.0] * 5, np.float32), dtype)
+    w = inputs.Workload("edges", "sum", dtype, 3, p0.size, p0.size, [p0, p1, p2])
+    assert_bitexact(run_sum(w), ref_sum(w), dtype, "edges vector")
+    assert_bitexact(run_sum(w, [1, 0, 0]), ref_sum(w), dtype, "edges element")
+
+
+def test_sum_deterministic_and_on_a_side_stream():
+    w = inputs.random_sum("bf16", 4, 1 << 20, 9)
+    parts = [dev(p, "bf16") for p in w.partials]
+    s = torch.cuda.Stream()
+    outs = []
+    with torch.cuda.stream(s):
+        for _ in range(10):
+            o = torch.empty_like(parts[0])
+            ar.ar_sum(parts, o, stream=s)
+            outs.append(o)
+    s.synchronize()
+    first = host_bits(outs[0])
+    assert_bitexact(first, ref_sum(w), "bf16", "side stream")
+    for o in outs[1:]:
+        assert np.array_equal(host_bits(o), first)
+
+
+# ------------------------------------------------------------ fused op
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("hidden", [8, 64, 520, 4096, 4100, 5120, 8192, 16384, 20480, 65536])
+def test_fused_widths(dtype, hidden):
+    """Register-row kernel (16-byte rows up to 8 packs per lane), the wide
+    two-pass vector kernel beyond, and the element kernel for rows whose byte
+    size is not a multiple of 16 (4100 fp16/bf16, 520 is fine)."""
+    for rows in (1, 7, 33):
+        if rows * hidden > 1 << 21:
+            continue
+        note(f"[parity] fused {dtype} H={hidden} rows={rows}")
+        w = inputs.random_fused(dtype, 2, rows, hidden, 300 + rows)
+        got_out, got_inter = run_fused(w)
+        check_fused(w, got_out, got_inter)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ranks", range(1, 9))
+def test_fused_ranks(dtype, ranks):
+    note(f"[parity] fused {dtype} R={ranks}")
+    w = inputs.random_fused(dtype, ranks, 9, 2048, 500 + ranks)
+    got_out, got_inter = run_fused(w)
+    check_fused(w, got_out, got_inter)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("bias,residual", [(False, False), (True, False), (False, True)])
+def test_fused_optional_terms(dtype, bias, residual):
+    for hidden in (1024, 4100):
+        note(f"[parity] fused {dtype} bias={bias} residual={residual} H={hidden}")
+        w = inputs.random_fused(dtype, 3, 5, hidden, 600, bias=bias, residual=residual)
+        got_out, got_inter = run_fused(w)
+        check_fused(w, got_out, got_inter)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_fused_aliasing(dtype):
+    """intermediate == residual (S replaces the residual in place), and
+    output == a partial."""
+    w = inputs.random_fused(dtype, 4, 6, 4096, 700)
+    ref_out, ref_inter = ref_fused(w)
+    parts = [dev(p, dtype) for p in w.partials]
+    res = dev(w.residual, dtype)
+    ar.ar_residual_rmsnorm(parts, dev(w.weight, dtype), w.eps, parts[1], res, bias=dev(w.bias, dtype),
+                           residual=res)
+    torch.cuda.synchronize()
+    assert_bitexact(host_bits(res), ref_inter, dtype, "intermediate in place of the residual")
+    assert_output_close(host_bits(parts[1]), ref_out, dtype, "output in place of partial 1")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_fused_unaligned_pointers(dtype):
+    w = inputs.random_fused(dtype, 2, 4, 1024, 800)
+    parts = []
+    for r, p in enumerate(w.partials):
+        t = torch.empty(w.n + 1 + r, dtype=TORCH_DT[dtype], device="cuda")
+        t[1 + r:].copy_(dev(p, dtype))
+        parts.append(t[1 + r:])
+    out, inter = Guarded(w.n, dtype, 1), Guarded(w.n, dtype, 2)
+    ar.ar_residual_rmsnorm(parts, dev(w.weight, dtype), w.eps, out.t, inter.t, bias=dev(w.bias, dtype),
+                           residual=dev(w.residual, dtype))
+    torch.cuda.synchronize()
+    out.check_guards()
+    inter.check_guards()
+    check_fused(w, host_bits(out.t), host_bits(inter.t))
+
+
+def test_fused_special_rows():
+    """Zero rows with eps > 0 give zeros; a constant row gives +-weight;
+    eps = 0 with a zero row gives NaN on both sides."""
+    H = 1024
+    for dtype in DTYPES:
+        zero = inputs.to_dtype(np.zeros(3 * H, np.float32), dtype)
+        const = inputs.to_dtype(np.full(3 * H, -0.75, np.float32), dtype)
+        weight = inputs.normal((H,), 3, 1.0, 0.1, dtype)
+        for parts, eps in (([zero, zero], 1e-6), ([const, zero], 0.0), ([zero], 0.0)):
+            w = inputs.Workload("special-rows", "fused", dtype, len(parts), 3 * H, H, parts, None, None, weight, eps)
+            got_out, got_inter = run_fused(w)
+            check_fused(w, got_out, got_inter)
+
+
+def test_fused_deterministic_at_full_size():
+    """The large fused workload, repeated: bitwise identical each time."""
+    w = inputs.make(inputs.FUSED_BF16_R8_2048x8192)
+    parts = [dev(p, w.dtype) for p in w.partials]
+    weight, res = dev(w.weight, w.dtype), dev(w.residual, w.dtype)
+    out, inter = torch.empty_like(parts[0]), torch.empty_like(parts[0])
+    first = None
+    for i in range(20):
+        ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, residual=res)
+        torch.cuda.synchronize()
+        b = host_bits(out)
+        if first is None:
+            first = b
+        else:
+            assert np.array_equal(b, first), f"run {i} differs"
+
+
+def test_raw_params_validation_on_device():
+    """Validation through the raw C ABI with real device buffers."""
+    t = torch.zeros(1024, device="cuda")
+    p = make_params(1024, 2, ar.AR_FP32, [t.data_ptr(), t.data_ptr() + 8], t.data_ptr() + 4)
+    assert call("ar_sum", p) == ar.ar.AR_ERR_ALIAS
+    p = make_params(1024, 2, ar.AR_FP32, [t.data_ptr(), t.data_ptr()], t.data_ptr() + 2)
+    assert call("ar_sum", p) == ar.ar.AR_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(t).item() == 0
