@@ -45,6 +45,7 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -88,20 +89,22 @@ __device__ __forceinline__ void st16(u32x4 *p, u32x4 v)
 
 // ------------------------------------------------------------- element types
 // V elements per 16-byte pack; widen() is exact; narrow() rounds to nearest even.
+// Bit casts act on whole vectors or on scalars held in variables, never on a
+// vector element expression (p.x), which bit_cast does not read correctly.
 struct Fp32 {
     static constexpr int V = 4;
     static constexpr int kSize = 4;
     __device__ static void widen(u32x4 p, float *f)
     {
-        f[0] = __builtin_bit_cast(float, p.x);
-        f[1] = __builtin_bit_cast(float, p.y);
-        f[2] = __builtin_bit_cast(float, p.z);
-        f[3] = __builtin_bit_cast(float, p.w);
+        const f32x4 v = __builtin_bit_cast(f32x4, p);
+        f[0] = v.x;
+        f[1] = v.y;
+        f[2] = v.z;
+        f[3] = v.w;
     }
     __device__ static u32x4 narrow(const float *f)
     {
-        return u32x4{__builtin_bit_cast(uint32_t, f[0]), __builtin_bit_cast(uint32_t, f[1]),
-                     __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3])};
+        return __builtin_bit_cast(u32x4, (f32x4{f[0], f[1], f[2], f[3]}));
     }
     __device__ static float load1(const void *b, size_t i) { return static_cast<const float *>(b)[i]; }
     // Rounds x to the type, stores it, and returns the stored value widened.
