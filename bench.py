@@ -6,8 +6,9 @@ One step = one ar_residual_rmsnorm call on the large fused workload: 8 bf16
 rank partials of [2048 tokens, 8192 hidden] summed in fp32, plus residual, then
 RMSNorm (eps 1e-5, no bias), writing the pre-norm sum and the normed output.
 Inputs are seeded synthetic data already resident in HBM. Steps rotate over
-several copies of the inputs so that each call streams from HBM rather than
-from the 256 MB last-level cache.
+enough copies of the inputs and outputs (at least 4x the 256 MB last-level
+cache in all, the outputs alone at least 2x) that each call streams from and
+to HBM rather than the cache.
 
 Prints ONE JSON line: effective HBM GB/s (algorithmic bytes / time), the
 roofline of the fused kernel against the 8 TB/s HBM peak, the standalone sum
@@ -69,9 +70,11 @@ def measured_traffic(kernel: str, workload: str):
     return entry.get("bytes_per_launch")
 
 
-def rotation_sets(bytes_per_set: int) -> int:
-    # enough copies that the cycle is more than twice the last-level cache
-    return max(2, -(-2 * LLC_BYTES // bytes_per_set) + 1)
+def rotation_sets(bytes_per_set: int, out_bytes_per_set: int) -> int:
+    """Copies of the inputs/outputs to cycle through: the whole cycle is at
+    least 4x the last-level cache and the outputs alone at least 2x, so that
+    neither inputs nor earlier outputs are served from cache."""
+    return max(2, -(-4 * LLC_BYTES // bytes_per_set), -(-2 * LLC_BYTES // out_bytes_per_set))
 
 
 def time_launches(torch, launch, nsets, steps, warmup, stream):
@@ -108,7 +111,7 @@ def dev(torch, a, dtype):
 
 def bench_fused(torch, ar, w, args, stream):
     nb = w.algorithmic_bytes()
-    nsets = rotation_sets(nb)
+    nsets = rotation_sets(nb, 2 * w.n * w.itemsize)
     base = [dev(torch, p, w.dtype) for p in w.partials]
     res0 = dev(torch, w.residual, w.dtype)
     weight = dev(torch, w.weight, w.dtype)
@@ -130,7 +133,7 @@ def bench_fused(torch, ar, w, args, stream):
 
 def bench_sum(torch, ar, w, args, stream):
     nb = w.algorithmic_bytes()
-    nsets = rotation_sets(nb)
+    nsets = rotation_sets(nb, w.n * w.itemsize)
     base = [dev(torch, p, w.dtype) for p in w.partials]
     sets = []
     for k in range(nsets):
@@ -219,9 +222,11 @@ def main():
 
     f = bench_fused(torch, ar, w, args, stream)
     gbps = f["bytes"] / (f["ms_step"] * 1e-3) / 1e9
-    achieved = f["bytes"] / (f["k_mean"] * 1e-3) / 1e9
-    print(f"[bench] fused: {f['ms_step'] * 1e3:.1f} us/step, kernel {f['k_mean'] * 1e3:.1f} us "
-          f"({achieved:.0f} GB/s)", file=sys.stderr, flush=True)
+    # One launch per step, back to back on one stream (no gaps between them):
+    # the region time per step is the average launch duration.
+    achieved = gbps
+    print(f"[bench] fused: {f['ms_step'] * 1e3:.1f} us/step ({achieved:.0f} GB/s); isolated launches "
+          f"{f['k_mean'] * 1e3:.1f} us", file=sys.stderr, flush=True)
     gpu_out, gpu_inter = host_bits(torch, f["out"]), host_bits(torch, f["inter"])
     del f["out"], f["inter"]
 
@@ -249,23 +254,24 @@ def main():
             "kernel": FUSED_KERNEL, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(FUSED_KERNEL, name),
-            "kernel_us_mean": round(f["k_mean"] * 1e3, 2), "kernel_us_median": round(f["k_med"] * 1e3, 2),
-            "kernel_us_min": round(f["k_min"] * 1e3, 2), "algorithmic_bytes_per_launch": f["bytes"],
+            "launch_us": round(f["ms_step"] * 1e3, 2), "algorithmic_bytes_per_launch": f["bytes"],
+            "isolated_launch_us": {"mean": round(f["k_mean"] * 1e3, 2), "median": round(f["k_med"] * 1e3, 2),
+                                   "min": round(f["k_min"] * 1e3, 2)},
         },
     }
 
     if not args.no_sum:
         sw = inputs.make(inputs.SUM_BF16_R4_8192x8192)
         s = bench_sum(torch, ar, sw, args, stream)
-        s_ach = s["bytes"] / (s["k_mean"] * 1e-3) / 1e9
+        s_ach = s["bytes"] / (s["ms_step"] * 1e-3) / 1e9
         result["standalone_sum"] = {
             "workload": sw.name, "kernel": SUM_KERNEL, "bytes_per_call": s["bytes"],
-            "us_per_call": round(s["ms_step"] * 1e3, 2), "kernel_us_mean": round(s["k_mean"] * 1e3, 2),
+            "us_per_call": round(s["ms_step"] * 1e3, 2), "isolated_launch_us_mean": round(s["k_mean"] * 1e3, 2),
             "gbps": round(s["bytes"] / (s["ms_step"] * 1e-3) / 1e9, 1), "achieved": round(s_ach, 1),
             "frac": round(s_ach / HBM_PEAK_GBPS, 4), "steps": s["steps"], "rotating_input_sets": s["nsets"],
             "traffic": measured_traffic(SUM_KERNEL, sw.name),
         }
-        print(f"[bench] sum: kernel {s['k_mean'] * 1e3:.1f} us ({s_ach:.0f} GB/s)", file=sys.stderr, flush=True)
+        print(f"[bench] sum: {s['ms_step'] * 1e3:.1f} us/call ({s_ach:.0f} GB/s)", file=sys.stderr, flush=True)
         del sw
 
     result["copy_ceiling_gbps"] = round(copy_ceiling(torch, stream), 1)

@@ -35,6 +35,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -52,18 +54,31 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPackBytes = 16;
 constexpr int kWave = 64;
-constexpr int kSumThreads = 256;        // workgroup size of the sum kernels
+// Tuning constants (compile-time; the defaults are the measured best).
+#ifndef AR_SUM_THREADS
+#define AR_SUM_THREADS 256              // workgroup size of the sum kernel
+#endif
 #ifndef AR_SUM_UNROLL
 #define AR_SUM_UNROLL 2                 // packs per lane per step of the sum
 #endif
+#ifndef AR_SUM_GRID_CAP
+#define AR_SUM_GRID_CAP 0               // 0: one workgroup per step; else at most this many
+#endif
 #ifndef AR_NT_LOADS
-#define AR_NT_LOADS 1                   // non-temporal (streaming) loads/stores
+#define AR_NT_LOADS 1                   // non-temporal (streaming) loads of the big buffers
 #endif
-#ifndef AR_FUSED_THREADS
-#define AR_FUSED_THREADS 256            // preferred workgroup size of the fused kernel
+#ifndef AR_NT_STORES
+#define AR_NT_STORES 1                  // non-temporal (streaming) stores
 #endif
-constexpr int kMaxPPT = 8;              // packs per lane a fused row may hold in registers
-constexpr int kFusedMaxThreads = 256;   // launch bound of the register-row kernel
+constexpr int kSumThreads = AR_SUM_THREADS;
+// Register-row fused kernel: a row of up to 1024 packs takes 1 or 2 packs per
+// lane on up to 512 lanes; wider rows (up to 2048 packs) take 3..8 packs per
+// lane on up to 256 lanes, which keeps every variant within the VGPR budget of
+// its launch bound.
+constexpr int kMaxPPT = 8;
+constexpr int kFusedMaxThreads = 512;
+template <int PPT>
+constexpr int fused_bound() { return PPT <= 2 ? 512 : 256; }
 constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
 constexpr int kElemThreads = 256;       // element-wise kernels
 constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
@@ -80,7 +95,7 @@ __device__ __forceinline__ u32x4 ld16(const u32x4 *p)
 
 __device__ __forceinline__ void st16(u32x4 *p, u32x4 v)
 {
-#if AR_NT_LOADS
+#if AR_NT_STORES
     __builtin_nontemporal_store(v, p);
 #else
     *p = v;
@@ -371,15 +386,15 @@ __device__ __forceinline__ u32x4 normed_pack(u32x4 sp, float rstd, u32x4 wp)
     return E::narrow(o);
 }
 
-// Fused op, one row per workgroup (rows beyond the grid loop), for rows of
-// up to kMaxPPT * kFusedMaxThreads packs. Lane l holds packs l, l+T, ...,
+// Fused op, one row per workgroup at a time (the resident grid loops over the
+// rows), for rows of up to kMaxPPT * 256 packs. Lane l holds packs l, l+T, ...,
 // l+(PPT-1)T of the row (T = workgroup size), so each load instruction of a
 // wave covers 1 KiB contiguous. The rounded S stays in registers as packs
 // (4 VGPRs per pack) and the weight packs are loaded before the barrier.
 template <class E, int R, int PPT>
-__global__ __launch_bounds__(kFusedMaxThreads) void ar_rmsnorm_pack_kernel(FusedArgs a)
+__global__ __launch_bounds__(fused_bound<PPT>()) void ar_rmsnorm_pack_kernel(FusedArgs a)
 {
-    __shared__ float part[kFusedMaxThreads / kWave];
+    __shared__ float part[fused_bound<PPT>() / kWave];
     const u32x4 *bias = static_cast<const u32x4 *>(a.bias);
     const u32x4 *weight = static_cast<const u32x4 *>(a.weight);
     const int T = blockDim.x;
@@ -603,27 +618,29 @@ bool sum_vector_ok(const ar_params_t *p)
     return true;
 }
 
-// Packs per lane and workgroup size of the register-row kernel for a row of
-// `ppr` packs: PPT = ceil(ppr / AR_FUSED_THREADS) (at most kMaxPPT), then the
-// fewest whole waves that cover the row. Returns false (PPT = 0) when the row
-// needs more than kMaxPPT * kFusedMaxThreads packs: the wide kernel takes it.
+// Packs per lane (PPT) and workgroup size of the register-row kernel for a
+// row of `ppr` packs: 1 pack per lane up to 512 packs, 2 up to 1024, then
+// ceil(ppr / 256) up to kMaxPPT; the workgroup is the fewest whole waves that
+// cover the row. Returns false (PPT = 0) for rows of more than
+// kMaxPPT * 256 packs, which the wide kernel takes.
 bool fused_geometry(int ppr, int *ppt, int *threads)
 {
-    static_assert(AR_FUSED_THREADS >= kWave && AR_FUSED_THREADS <= kFusedMaxThreads, "fused workgroup size");
-    int k = (ppr + AR_FUSED_THREADS - 1) / AR_FUSED_THREADS;
-    if (k < 1)
+    int k;
+    if (ppr <= 512)
         k = 1;
-    if (k > kMaxPPT)
-        k = kMaxPPT;
-    int t = (ppr + k - 1) / k;
-    t = (t + kWave - 1) / kWave * kWave;
-    if (t > kFusedMaxThreads) {
+    else if (ppr <= 1024)
+        k = 2;
+    else
+        k = (ppr + 255) / 256;
+    if (k > kMaxPPT) {
         *ppt = 0;
         *threads = kWideThreads;
         return false;
     }
+    int t = (ppr + k - 1) / k;
+    t = (t + kWave - 1) / kWave * kWave;
     *ppt = k;
-    *threads = t;
+    *threads = t < kWave ? kWave : t;
     return true;
 }
 
@@ -676,7 +693,9 @@ int32_t launch_sum(const ar_params_t *p, hipStream_t stream, bool vec)
     if (vec) {
         a.npacks = a.n / E::V;
         const size_t step = static_cast<size_t>(kSumThreads) * AR_SUM_UNROLL;
-        const unsigned grid = clamp_grid(a.npacks / step);
+        unsigned grid = clamp_grid(a.npacks / step);
+        if (AR_SUM_GRID_CAP > 0 && grid > static_cast<unsigned>(AR_SUM_GRID_CAP))
+            grid = AR_SUM_GRID_CAP;
         if (log_enabled())
             fprintf(stderr, "[ar] sum pack R=%d V=%d n=%zu grid=%u block=%d unroll=%d\n", R, E::V, a.n, grid,
                     kSumThreads, AR_SUM_UNROLL);
@@ -690,9 +709,53 @@ int32_t launch_sum(const ar_params_t *p, hipStream_t stream, bool vec)
     return check_launch("ar_sum launch");
 }
 
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 256;
+    if (dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+// Resident workgroups per CU of `kernel` at `threads` per workgroup (cached
+// per kernel instantiation and workgroup size).
+template <class K>
+int resident_per_cu(K kernel, int threads, std::atomic<int> (&cache)[kFusedMaxThreads / kWave + 1])
+{
+    const int slot = threads / kWave;
+    int c = cache[slot].load(std::memory_order_relaxed);
+    if (c > 0)
+        return c;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0)
+        n = 1;
+    cache[slot].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// The register-row kernel runs as one resident wave of workgroups (CUs x
+// workgroups per CU) that loop over the rows: no second dispatch round, whose
+// refill leaves CUs idle.
 template <class E, int R, int PPT>
 void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, hipStream_t stream)
 {
+    static std::atomic<int> occ[kFusedMaxThreads / kWave + 1];
+    const size_t resident =
+        static_cast<size_t>(device_cus()) * resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT>, threads, occ);
+    if (grid > resident)
+        grid = static_cast<unsigned>(resident);
     hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT>), dim3(grid), dim3(threads), 0, stream, a);
 }
 

@@ -182,11 +182,12 @@ def test_sum_deterministic_and_on_a_side_stream():
 
 # ------------------------------------------------------------ fused op
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [8, 64, 520, 4096, 4100, 5120, 8192, 16384, 20480, 65536])
+@pytest.mark.parametrize("hidden", [8, 64, 520, 4096, 4100, 5120, 8192, 10240, 12288, 14336, 16384, 20480, 65536])
 def test_fused_widths(dtype, hidden):
-    """Register-row kernel (16-byte rows up to 8 packs per lane), the wide
-    two-pass vector kernel beyond, and the element kernel for rows whose byte
-    size is not a multiple of 16 (4100 fp16/bf16, 520 is fine)."""
+    """Register-row kernel (1 or 2 packs per lane up to 1024 packs a row,
+    3..8 beyond), the wide two-pass vector kernel past 2048 packs, and the
+    element kernel for rows whose byte size is not a multiple of 16 (4100
+    fp16/bf16)."""
     for rows in (1, 7, 33):
         if rows * hidden > 1 << 21:
             continue
