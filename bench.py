@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--workload", default=None, help="fused workload name (default: the large bf16 one)")
     ap.add_argument("--no-sum", action="store_true", help="skip the standalone-sum line item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the unfused and two-shot line items")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (repeats the sample)")
     return ap.parse_args()
 
@@ -146,6 +147,71 @@ def bench_sum(torch, ar, w, args, stream):
     steps = max(5, args.steps // 2)
     ms_step, k_mean, k_med, k_min = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
     return dict(bytes=nb, nsets=nsets, ms_step=ms_step, k_mean=k_mean, k_med=k_med, k_min=k_min, steps=steps)
+
+
+def bench_unfused(torch, ar, w, args, stream):
+    """The unfused path on the fused workload: ar_sum into a buffer X, then
+    ar_rmsnorm (residual, bias, norm) on X. Bytes: the sum's (R+1)*N*s, the
+    norm's (X + residual + S + out)*N*s plus weight (and bias)."""
+    s = w.itemsize
+    nb = (w.ranks + 1) * w.n * s + (1 + (w.residual is not None) + 2) * w.n * s \
+        + (1 + (w.bias is not None)) * w.hidden * s
+    nsets = rotation_sets(nb, 3 * w.n * s)
+    base = [dev(torch, p, w.dtype) for p in w.partials]
+    res0 = dev(torch, w.residual, w.dtype)
+    weight = dev(torch, w.weight, w.dtype)
+    bias = dev(torch, w.bias, w.dtype) if w.bias is not None else None
+    sets = []
+    for k in range(nsets):
+        parts = base if k == 0 else [p.clone() for p in base]
+        res = res0 if k == 0 else res0.clone()
+        sets.append((parts, res, torch.empty_like(res0), torch.empty_like(res0), torch.empty_like(res0)))
+
+    def launch(k):
+        parts, res, x, out, inter = sets[k]
+        ar.ar_sum(parts, x, stream=stream)
+        ar.ar_rmsnorm(x, weight, w.eps, out, inter, bias=bias, residual=res, stream=stream)
+
+    steps = max(5, args.steps // 2)
+    ms_step, *_ = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
+    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, steps=steps)
+
+
+def bench_slice(torch, ar, w, args, stream, num):
+    """One rank's share (slice 0 of `num`) of the two-shot split."""
+    s = w.itemsize
+    base = [dev(torch, p, w.dtype) for p in w.partials]
+    res0 = dev(torch, w.residual, w.dtype) if w.residual is not None else None
+    weight = dev(torch, w.weight, w.dtype) if w.weight is not None else None
+    out0, inter0 = torch.empty_like(base[0]), torch.empty_like(base[0])
+    params = ar.make_params(w.n, w.ranks, {"fp32": 0, "fp16": 1, "bf16": 2}[w.dtype], [t.data_ptr() for t in base],
+                            out0.data_ptr(), hidden_size=w.hidden,
+                            weight=weight.data_ptr() if weight is not None else 0,
+                            intermediate=inter0.data_ptr(), residual=res0.data_ptr() if res0 is not None else 0)
+    op = ar.AR_FUSION_NONE if w.op == "sum" else ar.AR_FUSION_RESIDUAL_RMS_NORM
+    st, b, e = ar.ar_slice_range(params, op, 0, num)
+    assert st == 0, ar.ar_status_string(st)
+    m = e - b
+    if w.op == "sum":
+        nb = (w.ranks + 1) * m * s
+    else:
+        nb = (w.ranks + 2 + (w.residual is not None)) * m * s + (1 + (w.bias is not None)) * w.hidden * s
+    nsets = rotation_sets(nb * num, (1 if w.op == "sum" else 2) * w.n * s)
+    sets = [(base, res0, out0, inter0)]
+    for k in range(1, nsets):
+        sets.append(([p.clone() for p in base], res0.clone() if res0 is not None else None,
+                     torch.empty_like(base[0]), torch.empty_like(base[0])))
+
+    def launch(k):
+        parts, res, out, inter = sets[k]
+        if w.op == "sum":
+            ar.ar_sum_slice(parts, out, 0, num, stream=stream)
+        else:
+            ar.ar_residual_rmsnorm_slice(parts, weight, w.eps, out, inter, 0, num, residual=res, stream=stream)
+
+    steps = max(5, args.steps // 2)
+    ms_step, *_ = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
+    return dict(bytes=nb, elements=m, nsets=nsets, ms_step=ms_step, steps=steps)
 
 
 def copy_ceiling(torch, stream):
@@ -273,6 +339,24 @@ def main():
         }
         print(f"[bench] sum: {s['ms_step'] * 1e3:.1f} us/call ({s_ach:.0f} GB/s)", file=sys.stderr, flush=True)
         del sw
+
+    if not args.no_next:
+        u = bench_unfused(torch, ar, w, args, stream)
+        result["unfused_baseline"] = {
+            "what": "ar_sum into a buffer, then ar_rmsnorm on it (two launches)",
+            "us_per_call": round(u["ms_step"] * 1e3, 2), "bytes_per_call": u["bytes"],
+            "gbps": round(u["bytes"] / (u["ms_step"] * 1e-3) / 1e9, 1),
+            "fused_us_per_call": round(f["ms_step"] * 1e3, 2),
+            "time_saved_by_fusion": round(1 - f["ms_step"] / u["ms_step"], 4),
+        }
+        print(f"[bench] unfused: {u['ms_step'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+        sl = bench_slice(torch, ar, w, args, stream, w.ranks)
+        result["two_shot_share"] = {
+            "what": f"slice 0 of {w.ranks} of the fused op (one rank's share of a two-shot split)",
+            "elements": sl["elements"], "bytes_per_call": sl["bytes"], "us_per_call": round(sl["ms_step"] * 1e3, 2),
+            "gbps": round(sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9, 1),
+        }
+        print(f"[bench] two-shot share: {sl['ms_step'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
 
     result["copy_ceiling_gbps"] = round(copy_ceiling(torch, stream), 1)
 

@@ -82,6 +82,7 @@ enum {
     AR_ERR_EPS = -5,    /* eps is NaN, infinite or negative                        */
     AR_ERR_ALIAS = -6,  /* an output partly overlaps an input or the other output  */
     AR_ERR_ALIGN = -7,  /* a buffer is not aligned to the element size             */
+    AR_ERR_SLICE = -8,  /* slice index or slice count out of range                 */
     AR_ERR_HIP = -100   /* a HIP launch or copy failed; see ar_last_hip_error()    */
 };
 
@@ -137,6 +138,41 @@ int32_t ar_sum(const ar_params_t *p, void *hip_stream);
  * bias or weight, and no partial overlap is allowed (AR_ERR_ALIAS).
  */
 int32_t ar_residual_rmsnorm(const ar_params_t *p, void *hip_stream);
+
+/*
+ * The unfused branch's norm step ("allreduce.d2": after the two-shot
+ * all-reduce, rms_norm_kernel_launcher -> rms_norm_kernel): the same op as
+ * ar_residual_rmsnorm with a single input, x = input_buffer_ptrs[0]:
+ * intermediate = T((x + bias) + residual), out = RMSNorm(intermediate) * weight.
+ * Together with ar_sum it forms the unfused path (sum to a buffer, then norm),
+ * the baseline that shows what fusion saves. Requires ranks == 1
+ * (AR_ERR_RANKS otherwise); other rules as ar_residual_rmsnorm.
+ */
+int32_t ar_rmsnorm(const ar_params_t *p, void *hip_stream);
+
+/*
+ * Two-shot work split on one GPU: the share of slice `slice` (0-based) of
+ * `num_slices` (1..1024; a two-shot all-reduce over R ranks uses R slices,
+ * "allreduce.d2" twoShotAllReduceKernel, "type.d2" elts_per_rank). The slice
+ * is written in place into the full output buffers, so running every slice
+ * leaves exactly the result of the unsliced call (the all-gather layout).
+ *   ar_sum_slice:              elements [begin, end) of ar_sum; slices are
+ *                              equal shares of ceil(N / S) elements rounded up
+ *                              to whole 16-byte packs (the last may be short
+ *                              or empty).
+ *   ar_residual_rmsnorm_slice: whole rows: equal shares of ceil(rows / S) rows.
+ * p describes the FULL buffers and is validated as for the unsliced call.
+ * A slice that is empty returns AR_OK without launching anything. Bad slice
+ * arguments return AR_ERR_SLICE.
+ */
+int32_t ar_sum_slice(const ar_params_t *p, int32_t slice, int32_t num_slices, void *hip_stream);
+int32_t ar_residual_rmsnorm_slice(const ar_params_t *p, int32_t slice, int32_t num_slices, void *hip_stream);
+
+/* Element range [*begin, *end) that the slice call above covers, for the
+ * given fusion op (an ar_fusion_op_t). Validates p like the matching call;
+ * makes no HIP call. */
+int32_t ar_slice_range(const ar_params_t *p, int32_t fusion_op, int32_t slice, int32_t num_slices, size_t *begin,
+                       size_t *end);
 
 /*
  * "allreduce.d2" configurationSupported: validates p for the given fusion op

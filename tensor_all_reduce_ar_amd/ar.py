@@ -10,9 +10,13 @@ Entry points, same names as the C ABI:
   ar_residual_rmsnorm(partials, weight, eps, out, intermediate,
                       bias=None, residual=None, hidden_size=None)
                                                           fusion op RESIDUAL_RMS_NORM
+  ar_rmsnorm(x, weight, eps, out, intermediate, ...)      the unfused path's norm step
+  ar_sum_slice / ar_residual_rmsnorm_slice(..., slice_index, num_slices)
+                                                          one share of a two-shot split
+  ar_slice_range(params, fusion_op, slice_index, num_slices)
   ar_configuration_supported(params, fusion_op), ar_workspace_size(params),
   ar_status_string(code), ar_last_hip_error()
-plus ``Params`` / ``make_params`` and ``call`` for raw-pointer use.
+plus ``Params`` / ``make_params``, ``call`` and ``call_slice`` for raw-pointer use.
 """
 from __future__ import annotations
 
@@ -27,11 +31,12 @@ AR_FP32, AR_FP16, AR_BF16 = 0, 1, 2
 AR_FUSION_NONE, AR_FUSION_RESIDUAL_RMS_NORM = 0, 1
 AR_OK = 0
 AR_ERR_NULL, AR_ERR_RANKS, AR_ERR_DTYPE, AR_ERR_SHAPE = -1, -2, -3, -4
-AR_ERR_EPS, AR_ERR_ALIAS, AR_ERR_ALIGN, AR_ERR_HIP = -5, -6, -7, -100
+AR_ERR_EPS, AR_ERR_ALIAS, AR_ERR_ALIGN, AR_ERR_SLICE, AR_ERR_HIP = -5, -6, -7, -8, -100
 
 # Every function include/ar.h declares.
-EXPORTS = ("ar_sum", "ar_residual_rmsnorm", "ar_configuration_supported", "ar_workspace_size",
-           "ar_status_string", "ar_last_hip_error")
+EXPORTS = ("ar_sum", "ar_residual_rmsnorm", "ar_rmsnorm", "ar_sum_slice", "ar_residual_rmsnorm_slice",
+           "ar_slice_range", "ar_configuration_supported", "ar_workspace_size", "ar_status_string",
+           "ar_last_hip_error")
 
 
 class FusionParams(ctypes.Structure):
@@ -83,6 +88,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ar_sum.restype = ctypes.c_int32
     L.ar_residual_rmsnorm.argtypes = [P, ctypes.c_void_p]
     L.ar_residual_rmsnorm.restype = ctypes.c_int32
+    L.ar_rmsnorm.argtypes = [P, ctypes.c_void_p]
+    L.ar_rmsnorm.restype = ctypes.c_int32
+    for name in ("ar_sum_slice", "ar_residual_rmsnorm_slice"):
+        getattr(L, name).argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        getattr(L, name).restype = ctypes.c_int32
+    L.ar_slice_range.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t),
+                                 ctypes.POINTER(ctypes.c_size_t)]
+    L.ar_slice_range.restype = ctypes.c_int32
     L.ar_configuration_supported.argtypes = [P, ctypes.c_int32]
     L.ar_configuration_supported.restype = ctypes.c_int32
     L.ar_workspace_size.argtypes = [P]
@@ -125,8 +138,21 @@ def make_params(elts_total: int, ranks: int, dtype: int, inputs: Sequence[int], 
 
 
 def call(fn: str, params: Params, stream: Optional[int] = None) -> int:
-    """Call ar_sum / ar_residual_rmsnorm with a filled Params; returns the status."""
+    """Call ar_sum / ar_residual_rmsnorm / ar_rmsnorm with a filled Params; returns the status."""
     return getattr(load(), fn)(ctypes.byref(params), ctypes.c_void_p(stream or 0))
+
+
+def call_slice(fn: str, params: Params, slice_index: int, num_slices: int, stream: Optional[int] = None) -> int:
+    """Call ar_sum_slice / ar_residual_rmsnorm_slice; returns the status."""
+    return getattr(load(), fn)(ctypes.byref(params), slice_index, num_slices, ctypes.c_void_p(stream or 0))
+
+
+def ar_slice_range(params: Params, fusion_op: int, slice_index: int, num_slices: int):
+    """(status, begin, end) of a slice; begin/end are element indices."""
+    b, e = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = load().ar_slice_range(ctypes.byref(params), fusion_op, slice_index, num_slices, ctypes.byref(b),
+                               ctypes.byref(e))
+    return st, b.value, e.value
 
 
 def ar_configuration_supported(params: Params, fusion_op: int) -> int:
@@ -167,14 +193,31 @@ def _stream_handle(stream) -> int:
 
 def ar_sum(partials: Sequence, out, stream=None) -> None:
     """out = sum of the partials (fusion op NONE), on `stream` (default: torch's current)."""
+    st = call("ar_sum", _sum_params(partials, out), _stream_handle(stream))
+    if st != AR_OK:
+        raise ArError(st, "ar_sum")
+
+
+def _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size) -> Params:
+    if not 1 <= len(partials) <= AR_MAX_RANKS:
+        raise ValueError(f"need 1..{AR_MAX_RANKS} partials, got {len(partials)}")
+    n, dt = out.numel(), out.dtype
+    H = int(hidden_size if hidden_size is not None else weight.numel())
+    ptrs = [_check(p, f"partial {r}", dt, n) for r, p in enumerate(partials)]
+    return make_params(
+        n, len(partials), _dtype_code(out), ptrs, _check(out, "out", dt, n), hidden_size=H,
+        weight=_check(weight, "weight", dt, H), eps=float(eps),
+        intermediate=_check(intermediate, "intermediate", dt, n),
+        bias=_check(bias, "bias", dt, H) if bias is not None else 0,
+        residual=_check(residual, "residual", dt, n) if residual is not None else 0)
+
+
+def _sum_params(partials, out) -> Params:
     if not 1 <= len(partials) <= AR_MAX_RANKS:
         raise ValueError(f"need 1..{AR_MAX_RANKS} partials, got {len(partials)}")
     n, dt = out.numel(), out.dtype
     ptrs = [_check(p, f"partial {r}", dt, n) for r, p in enumerate(partials)]
-    params = make_params(n, len(partials), _dtype_code(out), ptrs, _check(out, "out", dt, n))
-    st = call("ar_sum", params, _stream_handle(stream))
-    if st != AR_OK:
-        raise ArError(st, "ar_sum")
+    return make_params(n, len(partials), _dtype_code(out), ptrs, _check(out, "out", dt, n))
 
 
 def ar_residual_rmsnorm(partials: Sequence, weight, eps: float, out, intermediate, bias=None, residual=None,
@@ -182,17 +225,34 @@ def ar_residual_rmsnorm(partials: Sequence, weight, eps: float, out, intermediat
     """Fusion op RESIDUAL_RMS_NORM: intermediate = ((sum + bias) + residual),
     out = RMSNorm(intermediate) * weight over rows of hidden_size elements
     (default: the weight's length)."""
-    if not 1 <= len(partials) <= AR_MAX_RANKS:
-        raise ValueError(f"need 1..{AR_MAX_RANKS} partials, got {len(partials)}")
-    n, dt = out.numel(), out.dtype
-    H = int(hidden_size if hidden_size is not None else weight.numel())
-    ptrs = [_check(p, f"partial {r}", dt, n) for r, p in enumerate(partials)]
-    params = make_params(
-        n, len(partials), _dtype_code(out), ptrs, _check(out, "out", dt, n), hidden_size=H,
-        weight=_check(weight, "weight", dt, H), eps=float(eps),
-        intermediate=_check(intermediate, "intermediate", dt, n),
-        bias=_check(bias, "bias", dt, H) if bias is not None else 0,
-        residual=_check(residual, "residual", dt, n) if residual is not None else 0)
+    params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
     st = call("ar_residual_rmsnorm", params, _stream_handle(stream))
     if st != AR_OK:
         raise ArError(st, "ar_residual_rmsnorm")
+
+
+def ar_rmsnorm(x, weight, eps: float, out, intermediate, bias=None, residual=None,
+               hidden_size: Optional[int] = None, stream=None) -> None:
+    """The unfused path's norm step on one input x: intermediate =
+    (x + bias) + residual, out = RMSNorm(intermediate) * weight."""
+    params = _fused_params([x], weight, eps, out, intermediate, bias, residual, hidden_size)
+    st = call("ar_rmsnorm", params, _stream_handle(stream))
+    if st != AR_OK:
+        raise ArError(st, "ar_rmsnorm")
+
+
+def ar_sum_slice(partials: Sequence, out, slice_index: int, num_slices: int, stream=None) -> None:
+    """Slice `slice_index` of `num_slices` of ar_sum, written in place into out."""
+    st = call_slice("ar_sum_slice", _sum_params(partials, out), slice_index, num_slices, _stream_handle(stream))
+    if st != AR_OK:
+        raise ArError(st, "ar_sum_slice")
+
+
+def ar_residual_rmsnorm_slice(partials: Sequence, weight, eps: float, out, intermediate, slice_index: int,
+                              num_slices: int, bias=None, residual=None, hidden_size: Optional[int] = None,
+                              stream=None) -> None:
+    """Rows of slice `slice_index` of `num_slices` of ar_residual_rmsnorm, in place."""
+    params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
+    st = call_slice("ar_residual_rmsnorm_slice", params, slice_index, num_slices, _stream_handle(stream))
+    if st != AR_OK:
+        raise ArError(st, "ar_residual_rmsnorm_slice")

@@ -849,17 +849,11 @@ struct FusedLauncher {
     }
 };
 
-}  // namespace
 
-// ------------------------------------------------------------------- C ABI
-extern "C" {
 
-int32_t ar_sum(const ar_params_t *p, void *hip_stream)
+// The sum on already-validated params (any elts_total > 0).
+int32_t run_sum(const ar_params_t *p, hipStream_t stream)
 {
-    int32_t st = validate_sum(p);
-    if (st != AR_OK || p->elts_total == 0)
-        return st;
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (p->ranks == 1) {  // passthrough
         if (p->local_output_buffer_ptr == p->input_buffer_ptrs[0])
             return AR_OK;
@@ -874,14 +868,127 @@ int32_t ar_sum(const ar_params_t *p, void *hip_stream)
     return dispatch<SumLauncher>(p->dtype, p->ranks, p, stream, sum_vector_ok(p));
 }
 
+// The fused op on already-validated params (any elts_total > 0).
+int32_t run_fused(const ar_params_t *p, hipStream_t stream)
+{
+    int ppt = 0, threads = 0;
+    const bool vec = fused_vector_ok(p, &ppt, &threads);
+    return dispatch<FusedLauncher>(p->dtype, p->ranks, p, stream, vec, ppt, threads);
+}
+
+constexpr int32_t kMaxSlices = 1024;
+
+// Elements [begin, end) of slice `slice` of `num_slices` (two-shot split).
+// Sum: equal shares of ceil(N / S) elements rounded up to whole 16-byte
+// packs, so every slice of a 16-byte-aligned buffer starts 16-byte aligned.
+// Fused: equal shares of ceil(rows / S) whole rows.
+int32_t slice_range(const ar_params_t *p, int32_t fusion_op, int32_t slice, int32_t num_slices, size_t *begin,
+                    size_t *end)
+{
+    if (num_slices < 1 || num_slices > kMaxSlices || slice < 0 || slice >= num_slices)
+        return AR_ERR_SLICE;
+    const size_t S = static_cast<size_t>(num_slices), k = static_cast<size_t>(slice), n = p->elts_total;
+    if (fusion_op == AR_FUSION_NONE) {
+        const size_t unit = kPackBytes / elem_size(p->dtype);
+        const size_t per = ((n + S - 1) / S + unit - 1) / unit * unit;
+        *begin = k * per < n ? k * per : n;
+        *end = *begin + per < n ? *begin + per : n;
+        return AR_OK;
+    }
+    if (fusion_op != AR_FUSION_RESIDUAL_RMS_NORM)
+        return AR_ERR_SHAPE;
+    const size_t H = static_cast<size_t>(p->fusion_params.hidden_size);
+    const size_t rows = n / H, per = (rows + S - 1) / S;
+    const size_t r0 = k * per < rows ? k * per : rows;
+    const size_t r1 = r0 + per < rows ? r0 + per : rows;
+    *begin = r0 * H;
+    *end = r1 * H;
+    return AR_OK;
+}
+
+// Params restricted to elements [begin, end): every full-size buffer is
+// offset; bias and weight ([hidden]) are not.
+ar_params_t sliced(const ar_params_t *p, size_t begin, size_t end)
+{
+    ar_params_t q = *p;
+    const size_t off = begin * elem_size(p->dtype);
+    auto at = [off](const void *b) -> const void * {
+        return b ? static_cast<const void *>(static_cast<const char *>(b) + off) : nullptr;
+    };
+    for (int r = 0; r < p->ranks; ++r)
+        q.input_buffer_ptrs[r] = at(p->input_buffer_ptrs[r]);
+    q.local_output_buffer_ptr = const_cast<void *>(at(p->local_output_buffer_ptr));
+    q.fusion_params.residual_buffer = at(p->fusion_params.residual_buffer);
+    q.fusion_params.intermediate_buffer = const_cast<void *>(at(p->fusion_params.intermediate_buffer));
+    q.elts_total = end - begin;
+    return q;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------- C ABI
+extern "C" {
+
+int32_t ar_sum(const ar_params_t *p, void *hip_stream)
+{
+    int32_t st = validate_sum(p);
+    if (st != AR_OK || p->elts_total == 0)
+        return st;
+    return run_sum(p, static_cast<hipStream_t>(hip_stream));
+}
+
 int32_t ar_residual_rmsnorm(const ar_params_t *p, void *hip_stream)
 {
     int32_t st = validate_fused(p);
     if (st != AR_OK || p->elts_total == 0)
         return st;
-    int ppt = 0, threads = 0;
-    const bool vec = fused_vector_ok(p, &ppt, &threads);
-    return dispatch<FusedLauncher>(p->dtype, p->ranks, p, static_cast<hipStream_t>(hip_stream), vec, ppt, threads);
+    return run_fused(p, static_cast<hipStream_t>(hip_stream));
+}
+
+int32_t ar_rmsnorm(const ar_params_t *p, void *hip_stream)
+{
+    if (p && p->ranks != 1)
+        return AR_ERR_RANKS;
+    return ar_residual_rmsnorm(p, hip_stream);
+}
+
+int32_t ar_slice_range(const ar_params_t *p, int32_t fusion_op, int32_t slice, int32_t num_slices, size_t *begin,
+                       size_t *end)
+{
+    if (!begin || !end)
+        return AR_ERR_NULL;
+    int32_t st = fusion_op == AR_FUSION_RESIDUAL_RMS_NORM ? validate_fused(p)
+                 : fusion_op == AR_FUSION_NONE            ? validate_sum(p)
+                                                          : AR_ERR_SHAPE;
+    if (st != AR_OK)
+        return st;
+    return slice_range(p, fusion_op, slice, num_slices, begin, end);
+}
+
+int32_t ar_sum_slice(const ar_params_t *p, int32_t slice, int32_t num_slices, void *hip_stream)
+{
+    int32_t st = validate_sum(p);
+    if (st != AR_OK)
+        return st;
+    size_t b = 0, e = 0;
+    st = slice_range(p, AR_FUSION_NONE, slice, num_slices, &b, &e);
+    if (st != AR_OK || b == e)
+        return st;
+    const ar_params_t q = sliced(p, b, e);
+    return run_sum(&q, static_cast<hipStream_t>(hip_stream));
+}
+
+int32_t ar_residual_rmsnorm_slice(const ar_params_t *p, int32_t slice, int32_t num_slices, void *hip_stream)
+{
+    int32_t st = validate_fused(p);
+    if (st != AR_OK)
+        return st;
+    size_t b = 0, e = 0;
+    st = slice_range(p, AR_FUSION_RESIDUAL_RMS_NORM, slice, num_slices, &b, &e);
+    if (st != AR_OK || b == e)
+        return st;
+    const ar_params_t q = sliced(p, b, e);
+    return run_fused(&q, static_cast<hipStream_t>(hip_stream));
 }
 
 int32_t ar_configuration_supported(const ar_params_t *p, int32_t fusion_op)
@@ -921,6 +1028,7 @@ const char *ar_status_string(int32_t status)
     case AR_ERR_EPS: return "AR_ERR_EPS: eps is NaN, infinite or negative";
     case AR_ERR_ALIAS: return "AR_ERR_ALIAS: an output partly overlaps an input or the other output";
     case AR_ERR_ALIGN: return "AR_ERR_ALIGN: a buffer is not aligned to the element size";
+    case AR_ERR_SLICE: return "AR_ERR_SLICE: slice index or slice count out of range";
     case AR_ERR_HIP: return "AR_ERR_HIP: a HIP call failed (see ar_last_hip_error)";
     default: return "unknown ar status";
     }

@@ -57,6 +57,7 @@ int main(void) {
          AR_OK, AR_ERR_NULL, AR_ERR_RANKS, AR_ERR_DTYPE, AR_ERR_SHAPE);
   printf("enum.AR_ERR_EPS %d\nenum.AR_ERR_ALIAS %d\nenum.AR_ERR_ALIGN %d\nenum.AR_ERR_HIP %d\n",
          AR_ERR_EPS, AR_ERR_ALIAS, AR_ERR_ALIGN, AR_ERR_HIP);
+  printf("enum.AR_ERR_SLICE %d\n", AR_ERR_SLICE);
   return 0;
 }
 ''')
@@ -77,7 +78,7 @@ def test_ctypes_mirrors_match_the_header(tmp_path):
         assert c[f"ar_fusion_params_t.{f}"] == getattr(ar.FusionParams, f).offset, f
     for name in ("AR_MAX_RANKS", "AR_FP32", "AR_FP16", "AR_BF16", "AR_FUSION_NONE", "AR_FUSION_RESIDUAL_RMS_NORM",
                  "AR_OK", "AR_ERR_NULL", "AR_ERR_RANKS", "AR_ERR_DTYPE", "AR_ERR_SHAPE", "AR_ERR_EPS",
-                 "AR_ERR_ALIAS", "AR_ERR_ALIGN", "AR_ERR_HIP"):
+                 "AR_ERR_ALIAS", "AR_ERR_ALIGN", "AR_ERR_SLICE", "AR_ERR_HIP"):
         assert c[f"enum.{name}"] == getattr(ar, name), name
 
 
@@ -206,7 +207,7 @@ def test_alignment_rules():
 def test_workspace_and_status_strings():
     assert ar.ar_workspace_size(sum_params()) == 0
     assert ar.ar_workspace_size(None) == 0
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -100, 1, -99, 12345):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -100, 1, -99, 12345):
         s = ar.ar_status_string(code)
         assert isinstance(s, str) and s
     assert ar.ar_status_string(ar.AR_ERR_ALIAS).startswith("AR_ERR_ALIAS")
@@ -245,3 +246,66 @@ def test_torch_front_end_checks_arguments():
         ar.ar_sum([x, x], x)  # host tensors are not device buffers
     with pytest.raises(ValueError):
         ar.ar_sum([], x)
+
+
+# ------------------------------------------------- two-shot slices (host)
+@pytest.mark.parametrize("dtype,size", [(ar.AR_FP32, 4), (ar.AR_FP16, 2), (ar.AR_BF16, 2)])
+@pytest.mark.parametrize("n", [1, 7, 8, 100, 1000003, 8192 * 8192])
+@pytest.mark.parametrize("num", [1, 2, 3, 4, 7, 8])
+def test_sum_slices_partition_with_aligned_starts(dtype, size, n, num):
+    """Slices cover [0, N) in order without gaps or overlap; each starts on a
+    16-byte boundary; all but the last non-empty one have the same length."""
+    p = sum_params(n=n, dtype=dtype)
+    ranges = []
+    for k in range(num):
+        st, b, e = ar.ar_slice_range(p, ar.AR_FUSION_NONE, k, num)
+        assert st == ar.AR_OK
+        ranges.append((b, e))
+    assert ranges[0][0] == 0 and ranges[-1][1] == n
+    for (b0, e0), (b1, e1) in zip(ranges, ranges[1:]):
+        assert e0 == b1 and b1 <= e1
+    for b, e in ranges:
+        if e > b:  # empty trailing slices sit at N
+            assert (b * size) % 16 == 0
+    lens = [e - b for b, e in ranges if e > b]
+    assert len(set(lens[:-1])) <= 1 and lens[-1] <= lens[0]
+    assert lens[0] >= -(-n // num)  # at least the even share (the elts_per_rank of a two-shot split)
+
+
+@pytest.mark.parametrize("rows,num", [(1, 1), (1, 8), (7, 2), (2048, 8), (4096, 3), (33, 8)])
+def test_fused_slices_are_whole_rows(rows, num):
+    H = 1024
+    p = fused_params(n=rows * H, hidden=H)
+    covered = 0
+    for k in range(num):
+        st, b, e = ar.ar_slice_range(p, ar.AR_FUSION_RESIDUAL_RMS_NORM, k, num)
+        assert st == ar.AR_OK and b == covered and b % H == 0 and e % H == 0 and e >= b
+        covered = e
+    assert covered == rows * H
+
+
+def test_slice_arguments_validated():
+    p = sum_params()
+    for k, num in ((0, 0), (-1, 2), (2, 2), (0, 1025)):
+        assert ar.ar_slice_range(p, ar.AR_FUSION_NONE, k, num)[0] == ar.AR_ERR_SLICE
+        assert ar.call_slice("ar_sum_slice", p, k, num) == ar.AR_ERR_SLICE
+        assert ar.call_slice("ar_residual_rmsnorm_slice", fused_params(), k, num) == ar.AR_ERR_SLICE
+    # the full params are validated first
+    assert ar.call_slice("ar_sum_slice", sum_params(ranks=9, inputs=[A] * 8), 0, 2) == ar.AR_ERR_RANKS
+    assert ar.call_slice("ar_residual_rmsnorm_slice", fused_params(hidden=0), 0, 2) == ar.AR_ERR_SHAPE
+    assert ar.ar_slice_range(p, 7, 0, 2)[0] == ar.AR_ERR_SHAPE
+
+
+def test_empty_slice_is_a_noop_without_any_hip_call():
+    # 10 bf16 elements in 8 slices: the share rounds up to one 16-byte pack (8
+    # elements), so slice 0 is [0, 8), slice 1 is [8, 10) and slices 2..7 are empty
+    p = sum_params(n=10, dtype=ar.AR_BF16)
+    assert ar.ar_slice_range(p, ar.AR_FUSION_NONE, 5, 8)[1:] == (10, 10)
+    assert ar.call_slice("ar_sum_slice", p, 5, 8) == ar.AR_OK
+    assert ar.call_slice("ar_residual_rmsnorm_slice", fused_params(n=2 * 1024, hidden=1024), 5, 8) == ar.AR_OK
+
+
+def test_rmsnorm_entry_needs_one_input():
+    assert ar.call("ar_rmsnorm", fused_params(ranks=2)) == ar.AR_ERR_RANKS
+    assert ar.call("ar_rmsnorm", fused_params(ranks=1, hidden=0)) == ar.AR_ERR_SHAPE
+    assert ar.load().ar_rmsnorm(None, None) == ar.AR_ERR_NULL

@@ -1,0 +1,163 @@
+"""GPU parity for the unfused baseline and the two-shot split on one GPU.
+
+Unfused path ("allreduce.d2", the branch that runs the all-reduce first and
+rms_norm_kernel after it): ar_sum writes the rounded sum X, then ar_rmsnorm
+adds bias and residual to X and normalizes. Its oracle is the same
+composition of oracle calls. Without bias and residual it equals the fused op
+bit for bit.
+
+Two-shot split ("allreduce.d2" twoShotAllReduceKernel; "type.d2"
+elts_per_rank): each slice call computes one rank's share in place in the full
+output; all slices together must equal the oracle's full result, and one
+slice must write exactly its range.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_all_reduce_ar_amd as ar
+from tensor_all_reduce_ar_amd import inputs
+
+from gpu_util import (Guarded, assert_bitexact, assert_output_close, bits, dev, empty_host, host_bits, note)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DTYPES = ("fp32", "fp16", "bf16")
+
+
+def oracle_sum(w):
+    ref = empty_host(w.n, w.dtype)
+    oracle.ar_sum(w.dtype, w.partials, ref)
+    return ref
+
+
+def oracle_fused(w, parts=None):
+    out, inter = empty_host(w.n, w.dtype), empty_host(w.n, w.dtype)
+    oracle.ar_residual_rmsnorm(w.dtype, parts if parts is not None else w.partials, w.hidden, w.weight, w.eps,
+                               out, inter, bias=w.bias, residual=w.residual)
+    return bits(out), bits(inter)
+
+
+# -------------------------------------------------------- unfused baseline
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ranks", [1, 2, 8])
+def test_unfused_path_matches_the_oracle_composition(dtype, ranks):
+    note(f"[next] unfused {dtype} R={ranks}")
+    w = inputs.random_fused(dtype, ranks, 12, 2048, 900 + ranks)
+    parts = [dev(p, dtype) for p in w.partials]
+    x = torch.empty_like(parts[0])
+    ar.ar_sum(parts, x)
+    out, inter = Guarded(w.n, dtype), Guarded(w.n, dtype)
+    ar.ar_rmsnorm(x, dev(w.weight, dtype), w.eps, out.t, inter.t, bias=dev(w.bias, dtype),
+                  residual=dev(w.residual, dtype))
+    torch.cuda.synchronize()
+    out.check_guards()
+    inter.check_guards()
+    xs = oracle_sum(w)
+    assert_bitexact(host_bits(x), bits(xs), dtype, "unfused sum")
+    ref_out, ref_inter = oracle_fused(w, parts=[xs])
+    assert_bitexact(host_bits(inter.t), ref_inter, dtype, "unfused intermediate")
+    assert_output_close(host_bits(out.t), ref_out, dtype, "unfused output")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_unfused_equals_fused_without_bias_and_residual(dtype):
+    w = inputs.random_fused(dtype, 4, 9, 4096, 950, bias=False, residual=False)
+    parts = [dev(p, dtype) for p in w.partials]
+    weight = dev(w.weight, dtype)
+    x = torch.empty_like(parts[0])
+    ar.ar_sum(parts, x)
+    out_u, inter_u = torch.empty_like(x), torch.empty_like(x)
+    ar.ar_rmsnorm(x, weight, w.eps, out_u, inter_u)
+    out_f, inter_f = torch.empty_like(x), torch.empty_like(x)
+    ar.ar_residual_rmsnorm(parts, weight, w.eps, out_f, inter_f)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(inter_u), host_bits(inter_f))
+    assert np.array_equal(host_bits(out_u), host_bits(out_f))
+
+
+# ---------------------------------------------------------- two-shot split
+def _slices(p_fn, fusion_op, num):
+    return [ar.ar_slice_range(p_fn(), fusion_op, k, num)[1:] for k in range(num)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("num", [2, 3, 4, 8])
+def test_sum_slices_compose_to_the_full_sum(dtype, num):
+    for n in (1, 100, 100003):
+        note(f"[next] sum slices {dtype} n={n} S={num}")
+        w = inputs.random_sum(dtype, 4, n, 1200 + num)
+        parts = [dev(p, dtype) for p in w.partials]
+        out = Guarded(n, dtype)
+        for k in range(num):
+            ar.ar_sum_slice(parts, out.t, k, num)
+        torch.cuda.synchronize()
+        out.check_guards()
+        assert_bitexact(host_bits(out.t), bits(oracle_sum(w)), dtype, f"sum slices n={n} S={num}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_one_sum_slice_writes_exactly_its_range(dtype):
+    n, num = 50000, 8
+    w = inputs.random_sum(dtype, 3, n, 1300)
+    parts = [dev(p, dtype) for p in w.partials]
+    ref = bits(oracle_sum(w))
+    for k in (0, 3, 7):
+        out = Guarded(n, dtype)
+        before = host_bits(out.t)
+        ar.ar_sum_slice(parts, out.t, k, num)
+        torch.cuda.synchronize()
+        out.check_guards()
+        params = ar.make_params(n, 3, {"fp32": 0, "fp16": 1, "bf16": 2}[dtype], [p.data_ptr() for p in parts],
+                                out.t.data_ptr())
+        st, b, e = ar.ar_slice_range(params, ar.AR_FUSION_NONE, k, num)
+        assert st == 0 and e > b
+        got = host_bits(out.t)
+        assert_bitexact(got[b:e], ref[b:e], dtype, f"slice {k}")
+        assert np.array_equal(got[:b], before[:b]) and np.array_equal(got[e:], before[e:])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("num", [2, 8])
+def test_fused_slices_compose_to_the_full_op(dtype, num):
+    w = inputs.random_fused(dtype, 4, 33, 1024, 1400 + num)
+    parts = [dev(p, dtype) for p in w.partials]
+    weight, bias, res = dev(w.weight, dtype), dev(w.bias, dtype), dev(w.residual, dtype)
+    out, inter = Guarded(w.n, dtype), Guarded(w.n, dtype)
+    for k in range(num):
+        ar.ar_residual_rmsnorm_slice(parts, weight, w.eps, out.t, inter.t, k, num, bias=bias, residual=res)
+    full_out, full_inter = torch.empty_like(parts[0]), torch.empty_like(parts[0])
+    ar.ar_residual_rmsnorm(parts, weight, w.eps, full_out, full_inter, bias=bias, residual=res)
+    torch.cuda.synchronize()
+    out.check_guards()
+    inter.check_guards()
+    ref_out, ref_inter = oracle_fused(w)
+    assert_bitexact(host_bits(inter.t), ref_inter, dtype, "fused slices intermediate")
+    assert_output_close(host_bits(out.t), ref_out, dtype, "fused slices output")
+    # each row runs the same code either way: bit-identical to the unsliced call
+    assert np.array_equal(host_bits(out.t), host_bits(full_out))
+
+
+def test_two_shot_split_at_the_large_shapes():
+    """Eight slices of the large fused workload and four of the large sum
+    compose to the oracle's full results."""
+    w = inputs.make(inputs.FUSED_BF16_R8_2048x8192)
+    parts = [dev(p, w.dtype) for p in w.partials]
+    weight, res = dev(w.weight, w.dtype), dev(w.residual, w.dtype)
+    out, inter = torch.empty_like(parts[0]), torch.empty_like(parts[0])
+    for k in range(8):
+        ar.ar_residual_rmsnorm_slice(parts, weight, w.eps, out, inter, k, 8, residual=res)
+    torch.cuda.synchronize()
+    ref_out, ref_inter = oracle_fused(w)
+    assert_bitexact(host_bits(inter), ref_inter, w.dtype, "large fused, 8 slices, intermediate")
+    assert_output_close(host_bits(out), ref_out, w.dtype, "large fused, 8 slices, output")
+    del parts, out, inter
+    s = inputs.make(inputs.SUM_BF16_R4_8192x8192)
+    sp = [dev(p, s.dtype) for p in s.partials]
+    so = torch.empty_like(sp[0])
+    for k in range(4):
+        ar.ar_sum_slice(sp, so, k, 4)
+    torch.cuda.synchronize()
+    assert_bitexact(host_bits(so), bits(oracle_sum(s)), s.dtype, "large sum, 4 slices")
