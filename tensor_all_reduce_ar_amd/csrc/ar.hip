@@ -56,7 +56,7 @@ constexpr int kPackBytes = 16;
 constexpr int kWave = 64;
 // Tuning constants (compile-time; the defaults are the measured best).
 #ifndef AR_SUM_THREADS
-#define AR_SUM_THREADS 256              // workgroup size of the sum kernel
+#define AR_SUM_THREADS 512              // workgroup size of the sum kernel
 #endif
 #ifndef AR_SUM_UNROLL
 #define AR_SUM_UNROLL 2                 // packs per lane per step of the sum
