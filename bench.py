@@ -214,6 +214,59 @@ def bench_slice(torch, ar, w, args, stream, num):
     return dict(bytes=nb, elements=m, nsets=nsets, ms_step=ms_step, steps=steps)
 
 
+def small_op_latency(torch, ar, inputs, stream, calls=20, reps=10):
+    """Per-call time of the launch-bound workloads, eager (back-to-back
+    launches) and replayed from a HIP graph of `calls` back-to-back calls,
+    which takes the host's launch cost out."""
+    names = [inputs.SUM_FP32_R2_4x256, inputs.FUSED_FP16_R8_16x4096, inputs.SUM_FP16_R2_1000003] + \
+        [inputs.fused_fp16_r2_5120_name(t) for t in (1, 7, 64)]
+    outl = {}
+    for name in names:
+        w = inputs.make(name)
+        parts = [dev(torch, p, w.dtype) for p in w.partials]
+        out = torch.empty_like(parts[0])
+        if w.op == "sum":
+            def call():
+                ar.ar_sum(parts, out)
+        else:
+            inter = torch.empty_like(parts[0])
+            weight, res = dev(torch, w.weight, w.dtype), dev(torch, w.residual, w.dtype)
+            bias = dev(torch, w.bias, w.dtype) if w.bias is not None else None
+
+            def call():
+                ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(calls * reps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        eager = a.elapsed_time(b) * 1e3 / (calls * reps)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(calls):
+                    call()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        graph = a.elapsed_time(b) * 1e3 / (calls * reps)
+        outl[name] = {"bytes": w.algorithmic_bytes(), "eager_us": round(eager, 2), "graph_us": round(graph, 2)}
+        del g
+    return outl
+
+
 def copy_ceiling(torch, stream):
     """A plain device copy of 1 GiB: read + write bytes over time."""
     n = 1 << 28  # fp32 elements, 1 GiB
@@ -357,6 +410,10 @@ def main():
             "gbps": round(sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9, 1),
         }
         print(f"[bench] two-shot share: {sl['ms_step'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+
+    if not args.no_next:
+        result["small_op_latency"] = small_op_latency(torch, ar, inputs, stream)
+        print("[bench] small-op latency done", file=sys.stderr, flush=True)
 
     result["copy_ceiling_gbps"] = round(copy_ceiling(torch, stream), 1)
 

@@ -168,3 +168,58 @@ def random_fused(dtype: str, ranks: int, rows: int, hidden: int, seed: int, eps:
     if not residual:
         w.residual = None
     return w
+
+
+# ------------------------------------------------- counter-based values
+# For arrays too large to draw on the host (indices past 2^31), element i of
+# stream `seed` is a function of (seed, i) alone, so the device can fill the
+# whole array and the host can recompute any sampled element. The hash is
+# SplitMix64's finalizer (Steele, Lea & Flood, "Fast splittable pseudorandom
+# number generators", OOPSLA 2014); its top 24 bits give a multiple of 2^-23
+# in [-1, 1), exactly representable in fp32 and rounded once to the element
+# type.
+_M64 = (1 << 64) - 1
+
+
+def _splitmix64(x):
+    """SplitMix64 finalizer on uint64 numpy arrays (wrapping arithmetic)."""
+    x = (x + np.uint64(0x9E3779B97F4A7C15))
+    x = (x ^ (x >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+    x = (x ^ (x >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return x ^ (x >> np.uint64(31))
+
+
+def counter_values(seed: int, idx: np.ndarray, dtype: str) -> np.ndarray:
+    """Values of stream `seed` at element indices `idx` (host, numpy)."""
+    with np.errstate(over="ignore"):
+        x = _splitmix64(np.asarray(idx, dtype=np.uint64) ^ np.uint64((seed * 0x632BE59BD9B4E019) & _M64))
+    top = (x >> np.uint64(40)).astype(np.int64)  # 24 bits
+    v = (top - (1 << 23)).astype(np.float32) * np.float32(2.0 ** -23)
+    return to_dtype(v, dtype)
+
+
+def counter_fill_device(seed: int, n: int, dtype: str, chunk: int = 1 << 26):
+    """The same stream for indices 0..n-1, built on the current torch device
+    chunk by chunk (torch int64 arithmetic wraps like uint64)."""
+    import torch
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    out = torch.empty(n, dtype=tdt, device="cuda")
+    key = (seed * 0x632BE59BD9B4E019) & _M64
+
+    def s64(v):  # uint64 constant as a wrapped int64
+        return v - (1 << 64) if v >= (1 << 63) else v
+
+    def srl(t, k):  # logical right shift of int64 holding uint64 bits
+        return (t >> k) & ((1 << (64 - k)) - 1)
+
+    for start in range(0, n, chunk):
+        m = min(chunk, n - start)
+        x = torch.arange(start, start + m, dtype=torch.int64, device="cuda") ^ s64(key)
+        x = x + s64(0x9E3779B97F4A7C15)
+        x = (x ^ srl(x, 30)) * s64(0xBF58476D1CE4E5B9)
+        x = (x ^ srl(x, 27)) * s64(0x94D049BB133111EB)
+        x = x ^ srl(x, 31)
+        top = srl(x, 40)
+        v = (top - (1 << 23)).to(torch.float32) * (2.0 ** -23)
+        out[start:start + m] = v.to(tdt)
+    return out
