@@ -40,8 +40,9 @@
  * weight and intermediate share the one dtype.
  *
  * Ownership and execution: the caller owns every buffer (device memory, e.g.
- * from torch). The library allocates nothing, keeps no state between calls and
- * needs no workspace. Calls are asynchronous on the caller's HIP stream
+ * from torch). The library allocates no device memory, keeps no state between
+ * calls that affects results (it caches the device's CU count and kernel
+ * occupancies) and needs no workspace. Calls are asynchronous on the caller's HIP stream
  * (NULL = the default stream): outputs are valid once the stream has been
  * synchronized. Calls are re-entrant and thread-safe.
  *
@@ -86,8 +87,8 @@ enum {
     AR_ERR_HIP = -100   /* a HIP launch or copy failed; see ar_last_hip_error()    */
 };
 
-/* Mirrors "type.d2" AllReduceFusionParams, field for field. Read only by
- * ar_residual_rmsnorm. */
+/* Mirrors "type.d2" AllReduceFusionParams, field for field. Read by the fused
+ * entry points (ar_residual_rmsnorm, ar_rmsnorm, ar_residual_rmsnorm_slice). */
 typedef struct {
     const void *bias_buffer;     /* [H] of T: the GEMM bias, added once per
                                     element after the rank sum. NULL = no bias. */
@@ -113,7 +114,7 @@ typedef struct {
                                                     rank order; entries >= R ignored   */
     void *local_output_buffer_ptr;               /* [elts_total] of T, OUTPUT. May be
                                                     one of the partials (in place).    */
-    ar_fusion_params_t fusion_params;            /* read by ar_residual_rmsnorm only   */
+    ar_fusion_params_t fusion_params;            /* read by the fused entry points     */
 } ar_params_t;
 
 /*

@@ -288,3 +288,33 @@ def test_raw_params_validation_on_device():
     assert call("ar_sum", p) == ar.ar.AR_ERR_ALIGN
     torch.cuda.synchronize()
     assert torch.count_nonzero(t).item() == 0
+
+
+def test_concurrent_streams_do_not_interfere():
+    """The library keeps no per-call state on the device: two streams running
+    different entry points at the same time both match their references."""
+    a = inputs.random_fused("bf16", 8, 256, 8192, 1600)
+    b = inputs.random_sum("fp16", 4, 1 << 22, 1601)
+    ap = [dev(p, a.dtype) for p in a.partials]
+    aw, aq = dev(a.weight, a.dtype), dev(a.residual, a.dtype)
+    bp = [dev(p, b.dtype) for p in b.partials]
+    ref_out, ref_inter = torch.empty_like(ap[0]), torch.empty_like(ap[0])
+    ar.ar_residual_rmsnorm(ap, aw, a.eps, ref_out, ref_inter, residual=aq)
+    ref_sum = torch.empty_like(bp[0])
+    ar.ar_sum(bp, ref_sum)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(8):
+        o, i, s = torch.empty_like(ap[0]), torch.empty_like(ap[0]), torch.empty_like(bp[0])
+        with torch.cuda.stream(s1):
+            ar.ar_residual_rmsnorm(ap, aw, a.eps, o, i, residual=aq, stream=s1)
+        with torch.cuda.stream(s2):
+            ar.ar_sum(bp, s, stream=s2)
+        outs.append((o, i, s))
+    torch.cuda.synchronize()
+    want = (host_bits(ref_out), host_bits(ref_inter), host_bits(ref_sum))
+    for o, i, s in outs:
+        assert np.array_equal(host_bits(o), want[0])
+        assert np.array_equal(host_bits(i), want[1])
+        assert np.array_equal(host_bits(s), want[2])
