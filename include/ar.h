@@ -34,6 +34,9 @@
  *                         rstd(t) = 1 / sqrt( sum_h S[t,h]^2 / hidden_size + eps )
  *                         for row t = i / hidden_size, column h = i % hidden_size.
  *
+ * Device: every buffer of a call must be on the calling thread's current HIP
+ * device, where the kernels are launched (the stream must belong to it too).
+ *
  * Layout: every full-size buffer is a dense row-major [elts_total / H, H]
  * array of T (for ar_sum, simply elts_total contiguous elements); bias and
  * weight are [H]. All element types alike: inputs, outputs, bias, residual,

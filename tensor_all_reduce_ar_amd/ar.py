@@ -172,9 +172,11 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _check(t, name: str, dtype, numel: int):
+def _check(t, name: str, dtype, numel: int, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the output on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.dtype != dtype:
@@ -184,40 +186,53 @@ def _check(t, name: str, dtype, numel: int):
     return t.data_ptr()
 
 
-def _stream_handle(stream) -> int:
+def _stream_handle(stream, device) -> int:
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
+    elif stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the buffers on {device}")
     return int(stream.cuda_stream)
+
+
+def _run(fn, params, stream, device, slice_args=None) -> None:
+    """Launch on the buffers' device (the library uses the current one)."""
+    import torch
+    with torch.cuda.device(device):
+        h = _stream_handle(stream, device)
+        st = call(fn, params, h) if slice_args is None else call_slice(fn, params, *slice_args, h)
+    if st != AR_OK:
+        raise ArError(st, fn)
 
 
 def ar_sum(partials: Sequence, out, stream=None) -> None:
     """out = sum of the partials (fusion op NONE), on `stream` (default: torch's current)."""
-    st = call("ar_sum", _sum_params(partials, out), _stream_handle(stream))
-    if st != AR_OK:
-        raise ArError(st, "ar_sum")
+    _run("ar_sum", _sum_params(partials, out), stream, out.device)
 
 
 def _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size) -> Params:
     if not 1 <= len(partials) <= AR_MAX_RANKS:
         raise ValueError(f"need 1..{AR_MAX_RANKS} partials, got {len(partials)}")
     n, dt = out.numel(), out.dtype
+    optr = _check(out, "out", dt, n)
+    d = out.device
     H = int(hidden_size if hidden_size is not None else weight.numel())
-    ptrs = [_check(p, f"partial {r}", dt, n) for r, p in enumerate(partials)]
+    ptrs = [_check(p, f"partial {r}", dt, n, d) for r, p in enumerate(partials)]
     return make_params(
-        n, len(partials), _dtype_code(out), ptrs, _check(out, "out", dt, n), hidden_size=H,
-        weight=_check(weight, "weight", dt, H), eps=float(eps),
-        intermediate=_check(intermediate, "intermediate", dt, n),
-        bias=_check(bias, "bias", dt, H) if bias is not None else 0,
-        residual=_check(residual, "residual", dt, n) if residual is not None else 0)
+        n, len(partials), _dtype_code(out), ptrs, optr, hidden_size=H,
+        weight=_check(weight, "weight", dt, H, d), eps=float(eps),
+        intermediate=_check(intermediate, "intermediate", dt, n, d),
+        bias=_check(bias, "bias", dt, H, d) if bias is not None else 0,
+        residual=_check(residual, "residual", dt, n, d) if residual is not None else 0)
 
 
 def _sum_params(partials, out) -> Params:
     if not 1 <= len(partials) <= AR_MAX_RANKS:
         raise ValueError(f"need 1..{AR_MAX_RANKS} partials, got {len(partials)}")
     n, dt = out.numel(), out.dtype
-    ptrs = [_check(p, f"partial {r}", dt, n) for r, p in enumerate(partials)]
-    return make_params(n, len(partials), _dtype_code(out), ptrs, _check(out, "out", dt, n))
+    optr = _check(out, "out", dt, n)
+    ptrs = [_check(p, f"partial {r}", dt, n, out.device) for r, p in enumerate(partials)]
+    return make_params(n, len(partials), _dtype_code(out), ptrs, optr)
 
 
 def ar_residual_rmsnorm(partials: Sequence, weight, eps: float, out, intermediate, bias=None, residual=None,
@@ -226,9 +241,7 @@ def ar_residual_rmsnorm(partials: Sequence, weight, eps: float, out, intermediat
     out = RMSNorm(intermediate) * weight over rows of hidden_size elements
     (default: the weight's length)."""
     params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
-    st = call("ar_residual_rmsnorm", params, _stream_handle(stream))
-    if st != AR_OK:
-        raise ArError(st, "ar_residual_rmsnorm")
+    _run("ar_residual_rmsnorm", params, stream, out.device)
 
 
 def ar_rmsnorm(x, weight, eps: float, out, intermediate, bias=None, residual=None,
@@ -236,16 +249,12 @@ def ar_rmsnorm(x, weight, eps: float, out, intermediate, bias=None, residual=Non
     """The unfused path's norm step on one input x: intermediate =
     (x + bias) + residual, out = RMSNorm(intermediate) * weight."""
     params = _fused_params([x], weight, eps, out, intermediate, bias, residual, hidden_size)
-    st = call("ar_rmsnorm", params, _stream_handle(stream))
-    if st != AR_OK:
-        raise ArError(st, "ar_rmsnorm")
+    _run("ar_rmsnorm", params, stream, out.device)
 
 
 def ar_sum_slice(partials: Sequence, out, slice_index: int, num_slices: int, stream=None) -> None:
     """Slice `slice_index` of `num_slices` of ar_sum, written in place into out."""
-    st = call_slice("ar_sum_slice", _sum_params(partials, out), slice_index, num_slices, _stream_handle(stream))
-    if st != AR_OK:
-        raise ArError(st, "ar_sum_slice")
+    _run("ar_sum_slice", _sum_params(partials, out), stream, out.device, (slice_index, num_slices))
 
 
 def ar_residual_rmsnorm_slice(partials: Sequence, weight, eps: float, out, intermediate, slice_index: int,
@@ -253,6 +262,4 @@ def ar_residual_rmsnorm_slice(partials: Sequence, weight, eps: float, out, inter
                               stream=None) -> None:
     """Rows of slice `slice_index` of `num_slices` of ar_residual_rmsnorm, in place."""
     params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
-    st = call_slice("ar_residual_rmsnorm_slice", params, slice_index, num_slices, _stream_handle(stream))
-    if st != AR_OK:
-        raise ArError(st, "ar_residual_rmsnorm_slice")
+    _run("ar_residual_rmsnorm_slice", params, stream, out.device, (slice_index, num_slices))
