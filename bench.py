@@ -12,8 +12,10 @@ to HBM rather than the cache.
 
 Prints ONE JSON line: effective HBM GB/s (algorithmic bytes / time), the
 roofline of the fused kernel against the 8 TB/s HBM peak, the standalone sum
-on its large workload, a copy-kernel ceiling, and the CPU oracle timed on the
-host (its own baseline, single-threaded).
+on its large workload, the fused op on 4096 fp16 rows of 5120 (2 ranks, with
+bias), the unfused path and one two-shot share, the per-call latency of the
+small workloads, a copy-kernel ceiling, and the CPU oracle timed on the host
+(its own baseline, single-threaded).
 """
 from __future__ import annotations
 
@@ -307,6 +309,17 @@ def cpu_baseline(w, seconds):
     return t, len(times), out, inter
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def host_bits(torch, t):
     import numpy as np
     t = t.cpu()
@@ -412,6 +425,17 @@ def main():
         print(f"[bench] two-shot share: {sl['ms_step'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
 
     if not args.no_next:
+        mw = inputs.make(inputs.fused_fp16_r2_5120_name(4096))
+        m = bench_fused(torch, ar, mw, args, stream)
+        m_gbps = m["bytes"] / (m["ms_step"] * 1e-3) / 1e9
+        result["fused_fp16_r2_4096x5120"] = {
+            "workload": mw.name, "kernel": FUSED_KERNEL, "bytes_per_call": m["bytes"],
+            "us_per_call": round(m["ms_step"] * 1e3, 2), "gbps": round(m_gbps, 1),
+            "frac": round(m_gbps / HBM_PEAK_GBPS, 4), "rotating_input_sets": m["nsets"],
+        }
+        print(f"[bench] fused fp16 R=2 4096x5120: {m['ms_step'] * 1e3:.1f} us/call ({m_gbps:.0f} GB/s)",
+              file=sys.stderr, flush=True)
+        del mw, m
         result["small_op_latency"] = small_op_latency(torch, ar, inputs, stream)
         print("[bench] small-op latency done", file=sys.stderr, flush=True)
 
@@ -425,7 +449,7 @@ def main():
         result["cpu_baseline"] = {
             "value": round(w.algorithmic_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole {name} call ({w.rows} rows), {reps} run(s), median {t:.2f} s",
-            "host_cpu": platform.processor() or platform.machine(), "host_logical_cpus": os.cpu_count(),
+            "host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count(),
             "gpu_vs_oracle": {"intermediate_bitexact": bool(sig_ok), "output_max_ulp": ulp},
         }
         print(f"[bench] oracle: {t:.2f} s per call", file=sys.stderr, flush=True)

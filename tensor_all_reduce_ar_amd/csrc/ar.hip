@@ -71,14 +71,16 @@ constexpr int kWave = 64;
 #define AR_NT_STORES 1                  // non-temporal (streaming) stores
 #endif
 constexpr int kSumThreads = AR_SUM_THREADS;
-// Register-row fused kernel: a row of up to 1024 packs takes 1 or 2 packs per
-// lane on up to 512 lanes; wider rows (up to 2048 packs) take 3..8 packs per
-// lane on up to 256 lanes, which keeps every variant within the VGPR budget of
-// its launch bound.
+// Register-row fused kernel, two layouts. Throughput layout (more rows than
+// CUs): a row of up to 1024 packs takes 1 or 2 packs per lane on up to 512
+// lanes; wider rows (up to 2048 packs) take 3..8 packs per lane on up to 256
+// lanes, which keeps every variant within the VGPR budget of its launch bound.
+// Latency layout (no more rows than CUs, rows of 513..2048 packs): up to 1024
+// lanes, so each lane's packs - and so the memory round trips of a row - are
+// halved when the chip is not full anyway.
 constexpr int kMaxPPT = 8;
-constexpr int kFusedMaxThreads = 512;
-template <int PPT>
-constexpr int fused_bound() { return PPT <= 2 ? 512 : 256; }
+constexpr int kFusedMaxThreads = 1024;
+constexpr int kLatencyMaxPPT = 2;
 constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
 constexpr int kElemThreads = 256;       // element-wise kernels
 constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
@@ -391,10 +393,10 @@ __device__ __forceinline__ u32x4 normed_pack(u32x4 sp, float rstd, u32x4 wp)
 // l+(PPT-1)T of the row (T = workgroup size), so each load instruction of a
 // wave covers 1 KiB contiguous. The rounded S stays in registers as packs
 // (4 VGPRs per pack) and the weight packs are loaded before the barrier.
-template <class E, int R, int PPT>
-__global__ __launch_bounds__(fused_bound<PPT>()) void ar_rmsnorm_pack_kernel(FusedArgs a)
+template <class E, int R, int PPT, int BOUND>
+__global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
 {
-    __shared__ float part[fused_bound<PPT>() / kWave];
+    __shared__ float part[BOUND / kWave];
     const u32x4 *bias = static_cast<const u32x4 *>(a.bias);
     const u32x4 *weight = static_cast<const u32x4 *>(a.weight);
     const int T = blockDim.x;
@@ -618,33 +620,42 @@ bool sum_vector_ok(const ar_params_t *p)
     return true;
 }
 
-// Packs per lane (PPT) and workgroup size of the register-row kernel for a
-// row of `ppr` packs: 1 pack per lane up to 512 packs, 2 up to 1024, then
-// ceil(ppr / 256) up to kMaxPPT; the workgroup is the fewest whole waves that
-// cover the row. Returns false (PPT = 0) for rows of more than
-// kMaxPPT * 256 packs, which the wide kernel takes.
-bool fused_geometry(int ppr, int *ppt, int *threads)
+// Launch shape of the register-row kernel for a row of `ppr` packs.
+struct FusedGeometry {
+    int ppt;      // packs per lane; 0 = the row is too wide, the wide kernel takes it
+    int threads;  // workgroup size: the fewest whole waves that cover the row
+    int bound;    // launch bound of the kernel instance (512, 256 or 1024)
+};
+
+// Throughput layout: 1 pack per lane up to 512 packs, 2 up to 1024, then
+// ceil(ppr / 256) up to kMaxPPT. Latency layout (`few_rows`, rows of more than
+// 512 packs): ceil(ppr / 1024) packs per lane, up to kLatencyMaxPPT.
+FusedGeometry fused_geometry(int ppr, bool few_rows)
 {
-    int k;
-    if (ppr <= 512)
+    int k, bound;
+    if (few_rows && ppr > 512 && ppr <= kLatencyMaxPPT * kFusedMaxThreads) {
+        k = (ppr + kFusedMaxThreads - 1) / kFusedMaxThreads;
+        bound = kFusedMaxThreads;
+    } else if (ppr <= 512) {
         k = 1;
-    else if (ppr <= 1024)
+        bound = 512;
+    } else if (ppr <= 1024) {
         k = 2;
-    else
+        bound = 512;
+    } else {
         k = (ppr + 255) / 256;
-    if (k > kMaxPPT) {
-        *ppt = 0;
-        *threads = kWideThreads;
-        return false;
+        bound = 256;
     }
+    if (k > kMaxPPT)
+        return FusedGeometry{0, kWideThreads, kWideThreads};
     int t = (ppr + k - 1) / k;
     t = (t + kWave - 1) / kWave * kWave;
-    *ppt = k;
-    *threads = t < kWave ? kWave : t;
-    return true;
+    return FusedGeometry{k, t < kWave ? kWave : t, bound};
 }
 
-bool fused_vector_ok(const ar_params_t *p, int *ppt, int *threads)
+// The fused op can take the 16-byte pack kernels: row bytes a multiple of 16
+// and every buffer 16-byte aligned.
+bool fused_vector_ok(const ar_params_t *p)
 {
     const ar_fusion_params_t &f = p->fusion_params;
     const size_t s = elem_size(p->dtype);
@@ -658,8 +669,6 @@ bool fused_vector_ok(const ar_params_t *p, int *ppt, int *threads)
     for (int r = 0; r < p->ranks; ++r)
         if (!aligned(p->input_buffer_ptrs[r], kPackBytes))
             return false;
-    const size_t ppr = static_cast<size_t>(f.hidden_size) * s / kPackBytes;
-    fused_geometry(static_cast<int>(ppr), ppt, threads);
     return true;
 }
 
@@ -748,19 +757,19 @@ int resident_per_cu(K kernel, int threads, std::atomic<int> (&cache)[kFusedMaxTh
 // The register-row kernel runs as one resident wave of workgroups (CUs x
 // workgroups per CU) that loop over the rows: no second dispatch round, whose
 // refill leaves CUs idle.
-template <class E, int R, int PPT>
-void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, hipStream_t stream)
+template <class E, int R, int PPT, int BOUND>
+void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int cus, hipStream_t stream)
 {
     static std::atomic<int> occ[kFusedMaxThreads / kWave + 1];
     const size_t resident =
-        static_cast<size_t>(device_cus()) * resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT>, threads, occ);
+        static_cast<size_t>(cus) * resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT, BOUND>, threads, occ);
     if (grid > resident)
         grid = static_cast<unsigned>(resident);
-    hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT>), dim3(grid), dim3(threads), 0, stream, a);
+    hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT, BOUND>), dim3(grid), dim3(threads), 0, stream, a);
 }
 
 template <class E, int R>
-int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec, int ppt, int threads)
+int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
 {
     const ar_fusion_params_t &f = p->fusion_params;
     FusedArgs a = {};
@@ -775,27 +784,41 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec, int ppt
     a.rows = p->elts_total / static_cast<size_t>(f.hidden_size);
     a.eps = f.eps;
     const unsigned grid = clamp_grid(a.rows);
-    if (vec && ppt == 0) {
+    int cus = 0;
+    FusedGeometry g{0, 0, 0};
+    if (vec) {
         a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
+        cus = device_cus();
+        g = fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus));
+    }
+    if (vec && g.ppt == 0) {
         if (log_enabled())
             fprintf(stderr, "[ar] fused wide R=%d rows=%zu H=%d ppr=%d block=%d grid=%u\n", R, a.rows, a.hidden,
                     a.ppr, kWideThreads, grid);
         hipLaunchKernelGGL((ar_rmsnorm_wide_kernel<E, R>), dim3(grid), dim3(kWideThreads), 0, stream, a);
     } else if (vec) {
-        a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
         if (log_enabled())
-            fprintf(stderr, "[ar] fused pack R=%d rows=%zu H=%d ppr=%d ppt=%d block=%d grid=%u\n", R, a.rows,
-                    a.hidden, a.ppr, ppt, threads, grid);
-        switch (ppt) {
-        case 1: launch_fused_pack<E, R, 1>(a, grid, threads, stream); break;
-        case 2: launch_fused_pack<E, R, 2>(a, grid, threads, stream); break;
-        case 3: launch_fused_pack<E, R, 3>(a, grid, threads, stream); break;
-        case 4: launch_fused_pack<E, R, 4>(a, grid, threads, stream); break;
-        case 5: launch_fused_pack<E, R, 5>(a, grid, threads, stream); break;
-        case 6: launch_fused_pack<E, R, 6>(a, grid, threads, stream); break;
-        case 7: launch_fused_pack<E, R, 7>(a, grid, threads, stream); break;
-        case 8: launch_fused_pack<E, R, 8>(a, grid, threads, stream); break;
-        default: return AR_ERR_SHAPE;  // unreachable: fused_geometry yields 0..kMaxPPT
+            fprintf(stderr, "[ar] fused pack R=%d rows=%zu H=%d ppr=%d ppt=%d block=%d bound=%d grid=%u\n", R,
+                    a.rows, a.hidden, a.ppr, g.ppt, g.threads, g.bound, grid);
+        const int t = g.threads;
+        if (g.bound == kFusedMaxThreads) {
+            switch (g.ppt) {
+            case 1: launch_fused_pack<E, R, 1, kFusedMaxThreads>(a, grid, t, cus, stream); break;
+            case 2: launch_fused_pack<E, R, 2, kFusedMaxThreads>(a, grid, t, cus, stream); break;
+            default: return AR_ERR_SHAPE;  // unreachable: the latency layout yields 1..kLatencyMaxPPT
+            }
+        } else {
+            switch (g.ppt) {
+            case 1: launch_fused_pack<E, R, 1, 512>(a, grid, t, cus, stream); break;
+            case 2: launch_fused_pack<E, R, 2, 512>(a, grid, t, cus, stream); break;
+            case 3: launch_fused_pack<E, R, 3, 256>(a, grid, t, cus, stream); break;
+            case 4: launch_fused_pack<E, R, 4, 256>(a, grid, t, cus, stream); break;
+            case 5: launch_fused_pack<E, R, 5, 256>(a, grid, t, cus, stream); break;
+            case 6: launch_fused_pack<E, R, 6, 256>(a, grid, t, cus, stream); break;
+            case 7: launch_fused_pack<E, R, 7, 256>(a, grid, t, cus, stream); break;
+            case 8: launch_fused_pack<E, R, 8, 256>(a, grid, t, cus, stream); break;
+            default: return AR_ERR_SHAPE;  // unreachable: fused_geometry yields 0..kMaxPPT
+            }
         }
     } else {
         if (log_enabled())
@@ -841,9 +864,9 @@ struct SumLauncher {
 
 template <class E, int Unused>
 struct FusedLauncher {
-    static int32_t by_ranks(int ranks, const ar_params_t *p, hipStream_t s, bool vec, int ppt, int threads)
+    static int32_t by_ranks(int ranks, const ar_params_t *p, hipStream_t s, bool vec)
     {
-#define AR_CALL(R) launch_fused<E, R>(p, s, vec, ppt, threads)
+#define AR_CALL(R) launch_fused<E, R>(p, s, vec)
         AR_BY_RANKS(AR_CALL)
 #undef AR_CALL
     }
@@ -871,9 +894,7 @@ int32_t run_sum(const ar_params_t *p, hipStream_t stream)
 // The fused op on already-validated params (any elts_total > 0).
 int32_t run_fused(const ar_params_t *p, hipStream_t stream)
 {
-    int ppt = 0, threads = 0;
-    const bool vec = fused_vector_ok(p, &ppt, &threads);
-    return dispatch<FusedLauncher>(p->dtype, p->ranks, p, stream, vec, ppt, threads);
+    return dispatch<FusedLauncher>(p->dtype, p->ranks, p, stream, fused_vector_ok(p));
 }
 
 constexpr int32_t kMaxSlices = 1024;
@@ -1005,8 +1026,7 @@ int32_t ar_configuration_supported(const ar_params_t *p, int32_t fusion_op)
             return st;
         if (p->elts_total == 0)
             return 1;
-        int ppt = 0, threads = 0;
-        return fused_vector_ok(p, &ppt, &threads) ? 1 : 0;
+        return fused_vector_ok(p) ? 1 : 0;
     }
     return AR_ERR_SHAPE;
 }

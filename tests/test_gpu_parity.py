@@ -184,15 +184,29 @@ def test_sum_deterministic_and_on_a_side_stream():
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("hidden", [8, 64, 520, 4096, 4100, 5120, 8192, 10240, 12288, 14336, 16384, 20480, 65536])
 def test_fused_widths(dtype, hidden):
-    """Register-row kernel (1 or 2 packs per lane up to 1024 packs a row,
-    3..8 beyond), the wide two-pass vector kernel past 2048 packs, and the
-    element kernel for rows whose byte size is not a multiple of 16 (4100
-    fp16/bf16)."""
+    """Few rows: the register-row kernel in its latency layout (one pack per
+    lane up to 1024 packs a row, two up to 2048), the wide two-pass vector
+    kernel past 2048 packs, and the element kernel for rows whose byte size is
+    not a multiple of 16 (4100 fp16/bf16)."""
     for rows in (1, 7, 33):
         if rows * hidden > 1 << 21:
             continue
         note(f"[parity] fused {dtype} H={hidden} rows={rows}")
         w = inputs.random_fused(dtype, 2, rows, hidden, 300 + rows)
+        got_out, got_inter = run_fused(w)
+        check_fused(w, got_out, got_inter)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("hidden", [2048, 4096, 5120, 8192, 10240, 12288, 14336, 16384])
+def test_fused_widths_at_the_layout_switch(dtype, hidden):
+    """Up to one row per CU the register-row kernel takes its latency layout
+    (up to 1024 lanes a row); with more rows, its throughput layout (up to 512
+    lanes, 1..8 packs per lane). The row count at the switch and one past it."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for rows in (cus, cus + 1):
+        note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
+        w = inputs.random_fused(dtype, 8 if hidden >= 8192 else 3, rows, hidden, 350 + rows % 7)
         got_out, got_inter = run_fused(w)
         check_fused(w, got_out, got_inter)
 
