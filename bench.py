@@ -432,6 +432,7 @@ def main():
             "workload": mw.name, "kernel": FUSED_KERNEL, "bytes_per_call": m["bytes"],
             "us_per_call": round(m["ms_step"] * 1e3, 2), "gbps": round(m_gbps, 1),
             "frac": round(m_gbps / HBM_PEAK_GBPS, 4), "rotating_input_sets": m["nsets"],
+            "traffic": measured_traffic(FUSED_KERNEL, mw.name),
         }
         print(f"[bench] fused fp16 R=2 4096x5120: {m['ms_step'] * 1e3:.1f} us/call ({m_gbps:.0f} GB/s)",
               file=sys.stderr, flush=True)
