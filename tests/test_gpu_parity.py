@@ -108,7 +108,7 @@ def test_golden_small_workloads():
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("ranks", range(1, 9))
 def test_sum_sizes_and_tails(dtype, ranks):
-    for n in (1, 7, 8, 9, 17, 1027, 2 * 256 * 8 + 5, 70001):
+    for n in (1, 7, 8, 9, 15, 16, 17, 1027, 2 * 256 * 8 + 5, 70001):
         note(f"[parity] sum {dtype} R={ranks} n={n}")
         w = inputs.random_sum(dtype, ranks, n, 1000 + 10 * ranks + n % 97)
         assert_bitexact(run_sum(w), ref_sum(w), dtype, f"sum {dtype} R={ranks} n={n}")
@@ -121,6 +121,23 @@ def test_sum_unaligned_pointers(dtype):
         note(f"[parity] sum unaligned {dtype} offsets={offs} out={oo}")
         w = inputs.random_sum(dtype, 3, 4099, 77)
         assert_bitexact(run_sum(w, offs, oo), ref_sum(w), dtype, f"unaligned {offs}/{oo}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("byte_offset", [2, 4, 8])
+def test_sum_pointer_byte_offsets(dtype, byte_offset):
+    """Every buffer (partials and output) shifted by the same byte offset, for
+    the offsets that keep element alignment, over sizes with and without a
+    tail."""
+    size = 4 if dtype == "fp32" else 2
+    if byte_offset % size:
+        pytest.skip("offset breaks element alignment (rejected with AR_ERR_ALIGN)")
+    k = byte_offset // size
+    for ranks in (2, 5, 8):
+        for n in (16, 1027, 100003):
+            note(f"[parity] sum {dtype} R={ranks} n={n} byte offset {byte_offset}")
+            w = inputs.random_sum(dtype, ranks, n, 1500 + ranks + n % 89)
+            assert_bitexact(run_sum(w, [k] * ranks, k), ref_sum(w), dtype, f"offset {byte_offset} B R={ranks} n={n}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -188,7 +205,7 @@ def test_fused_widths(dtype, hidden):
     lane up to 1024 packs a row, two up to 2048), the wide two-pass vector
     kernel past 2048 packs, and the element kernel for rows whose byte size is
     not a multiple of 16 (4100 fp16/bf16)."""
-    for rows in (1, 7, 33):
+    for rows in (1, 7, 33, 64):
         if rows * hidden > 1 << 21:
             continue
         note(f"[parity] fused {dtype} H={hidden} rows={rows}")
@@ -277,20 +294,21 @@ def test_fused_special_rows():
 
 
 def test_fused_deterministic_at_full_size():
-    """The large fused workload, repeated: bitwise identical each time."""
+    """The large fused workload, 100 times: bitwise identical each time."""
     w = inputs.make(inputs.FUSED_BF16_R8_2048x8192)
     parts = [dev(p, w.dtype) for p in w.partials]
     weight, res = dev(w.weight, w.dtype), dev(w.residual, w.dtype)
     out, inter = torch.empty_like(parts[0]), torch.empty_like(parts[0])
     first = None
-    for i in range(20):
+    for i in range(100):
+        out.fill_(float("nan"))
         ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, residual=res)
         torch.cuda.synchronize()
-        b = host_bits(out)
+        b = (host_bits(out), host_bits(inter))
         if first is None:
             first = b
         else:
-            assert np.array_equal(b, first), f"run {i} differs"
+            assert np.array_equal(b[0], first[0]) and np.array_equal(b[1], first[1]), f"run {i} differs"
 
 
 def test_raw_params_validation_on_device():
