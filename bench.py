@@ -14,8 +14,11 @@ Prints ONE JSON line: effective HBM GB/s (algorithmic bytes / time), the
 roofline of the fused kernel against the 8 TB/s HBM peak, the standalone sum
 on its large workload, the fused op on 4096 fp16 rows of 5120 (2 ranks, with
 bias), the unfused path and one two-shot share, the per-call latency of the
-small workloads, a copy-kernel ceiling, and the CPU oracle timed on the host
-(its own baseline, single-threaded).
+small workloads, and the CPU oracle timed on the host (its own baseline). Each
+large workload also reports the streaming ceiling on its own buffers: the
+in-repo streaming kernel (libstream_ceiling.so) reading and writing exactly the
+same buffers once, with no other work; copy and read rates over 1 GiB are
+reported too.
 """
 from __future__ import annotations
 
@@ -130,8 +133,20 @@ def bench_fused(torch, ar, w, args, stream):
         ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res, stream=stream)
 
     ms_step, k_mean, k_med, k_min = time_launches(torch, launch, nsets, args.steps, args.warmup, stream)
+    out_bits, inter_bits = host_bits(torch, sets[0][2]), host_bits(torch, sets[0][3])
+
+    # The practical ceiling on the same buffers: every partial and the
+    # residual read once, S and the output written once, nothing else.
+    from tensor_all_reduce_ar_amd import stream_ceiling as sc
+
+    def stream_launch(k):
+        parts, res, out, inter = sets[k]
+        sc.sc_stream(list(parts) + ([res] if w.residual is not None else []), [inter, out], stream=stream)
+
+    ceil_ms, *_ = time_launches(torch, stream_launch, nsets, args.steps, args.warmup, stream)
+    ceil_bytes = (w.ranks + (w.residual is not None) + 2) * w.n * w.itemsize
     return dict(bytes=nb, nsets=nsets, ms_step=ms_step, k_mean=k_mean, k_med=k_med, k_min=k_min,
-                out=sets[0][2], inter=sets[0][3])
+                out_bits=out_bits, inter_bits=inter_bits, ceil_gbps=ceil_bytes / (ceil_ms * 1e-3) / 1e9)
 
 
 def bench_sum(torch, ar, w, args, stream):
@@ -148,7 +163,15 @@ def bench_sum(torch, ar, w, args, stream):
 
     steps = max(5, args.steps // 2)
     ms_step, k_mean, k_med, k_min = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
-    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, k_mean=k_mean, k_med=k_med, k_min=k_min, steps=steps)
+
+    from tensor_all_reduce_ar_amd import stream_ceiling as sc
+
+    def stream_launch(k):  # the same buffers, read and written once, nothing else
+        sc.sc_stream(sets[k][0], [sets[k][1]], stream=stream)
+
+    ceil_ms, *_ = time_launches(torch, stream_launch, nsets, steps, max(2, args.warmup // 2), stream)
+    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, k_mean=k_mean, k_med=k_med, k_min=k_min, steps=steps,
+                ceil_gbps=nb / (ceil_ms * 1e-3) / 1e9)
 
 
 def bench_unfused(torch, ar, w, args, stream):
@@ -269,23 +292,34 @@ def small_op_latency(torch, ar, inputs, stream, calls=20, reps=10):
     return outl
 
 
-def copy_ceiling(torch, stream):
-    """A plain device copy of 1 GiB: read + write bytes over time."""
+def stream_ceilings(torch, stream):
+    """Streaming rates over 1 GiB buffers: the in-repo streaming kernel as a
+    copy (1 read + 1 write stream) and as a pure read, and torch's own device
+    copy. GB/s of bytes moved."""
+    from tensor_all_reduce_ar_amd import stream_ceiling as sc
     n = 1 << 28  # fp32 elements, 1 GiB
     src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / 10
+
+    def rate(fn, nbytes, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+
+    out = {
+        "copy_gbps": rate(lambda: sc.sc_stream([src], [dst], stream=stream), 2 * n * 4),
+        "read_gbps": rate(lambda: sc.sc_stream([src], [], stream=stream), n * 4),
+        "torch_copy_gbps": rate(lambda: dst.copy_(src), 2 * n * 4),
+    }
     del src, dst
-    return 2 * n * 4 / (ms * 1e-3) / 1e9
+    return {k: round(v, 1) for k, v in out.items()}
 
 
 def cpu_baseline(w, seconds):
@@ -394,9 +428,9 @@ def main():
     # the region time per step is the average launch duration.
     achieved = gbps
     print(f"[bench] fused: {f['ms_step'] * 1e3:.1f} us/step ({achieved:.0f} GB/s); isolated launches "
-          f"{f['k_mean'] * 1e3:.1f} us", file=sys.stderr, flush=True)
-    gpu_out, gpu_inter = host_bits(torch, f["out"]), host_bits(torch, f["inter"])
-    del f["out"], f["inter"]
+          f"{f['k_mean'] * 1e3:.1f} us; streaming ceiling on the same buffers {f['ceil_gbps']:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    gpu_out, gpu_inter = f.pop("out_bits"), f.pop("inter_bits")
 
     result = {
         "metric": METRIC,
@@ -422,6 +456,8 @@ def main():
             "kernel": FUSED_KERNEL, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(FUSED_KERNEL, name),
+            "stream_ceiling_same_buffers": round(f["ceil_gbps"], 1),
+            "frac_of_stream_ceiling": round(achieved / f["ceil_gbps"], 4),
             "launch_us": round(f["ms_step"] * 1e3, 2), "algorithmic_bytes_per_launch": f["bytes"],
             "isolated_launch_us": {"mean": round(f["k_mean"] * 1e3, 2), "median": round(f["k_med"] * 1e3, 2),
                                    "min": round(f["k_min"] * 1e3, 2)},
@@ -438,6 +474,8 @@ def main():
             "gbps": round(s["bytes"] / (s["ms_step"] * 1e-3) / 1e9, 1), "achieved": round(s_ach, 1),
             "frac": round(s_ach / HBM_PEAK_GBPS, 4), "steps": s["steps"], "rotating_input_sets": s["nsets"],
             "traffic": measured_traffic(SUM_KERNEL, sw.name),
+            "stream_ceiling_same_buffers": round(s["ceil_gbps"], 1),
+            "frac_of_stream_ceiling": round(s_ach / s["ceil_gbps"], 4),
         }
         print(f"[bench] sum: {s['ms_step'] * 1e3:.1f} us/call ({s_ach:.0f} GB/s)", file=sys.stderr, flush=True)
         del sw
@@ -469,6 +507,8 @@ def main():
             "us_per_call": round(m["ms_step"] * 1e3, 2), "gbps": round(m_gbps, 1),
             "frac": round(m_gbps / HBM_PEAK_GBPS, 4), "rotating_input_sets": m["nsets"],
             "traffic": measured_traffic(FUSED_KERNEL, mw.name),
+            "stream_ceiling_same_buffers": round(m["ceil_gbps"], 1),
+            "frac_of_stream_ceiling": round(m_gbps / m["ceil_gbps"], 4),
         }
         print(f"[bench] fused fp16 R=2 4096x5120: {m['ms_step'] * 1e3:.1f} us/call ({m_gbps:.0f} GB/s)",
               file=sys.stderr, flush=True)
@@ -476,7 +516,9 @@ def main():
         result["small_op_latency"] = small_op_latency(torch, ar, inputs, stream)
         print("[bench] small-op latency done", file=sys.stderr, flush=True)
 
-    result["copy_ceiling_gbps"] = round(copy_ceiling(torch, stream), 1)
+    ceilings = stream_ceilings(torch, stream)
+    result["copy_ceiling_gbps"] = ceilings["copy_gbps"]
+    result["stream_ceilings_1gib"] = ceilings
 
     if not args.no_cpu_baseline:
         t, reps, ref_out, ref_inter = cpu_baseline(w, args.cpu_seconds)

@@ -1,8 +1,11 @@
-"""Build ``libar.so`` (the C-ABI library of HIP kernels) for gfx950, in-tree.
+"""Build the C-ABI libraries of HIP kernels for gfx950, in-tree.
 
     python -m tensor_all_reduce_ar_amd.build
 
-hipcc cross-compiles without a GPU. Extra ``-D`` definitions (tuning macros of
+``libar.so`` (csrc/ar.hip, include/ar.h) is the all-reduce core;
+``libstream_ceiling.so`` (csrc/stream_ceiling.hip, include/stream_ceiling.h)
+holds the streaming-ceiling kernels the benchmark times beside it. hipcc
+cross-compiles without a GPU. Extra ``-D`` definitions (tuning macros of
 csrc/ar.hip) can be passed through ``build(defines=...)``.
 """
 from __future__ import annotations
@@ -17,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "ar.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libar.so")
+CEILING_SRC = os.path.join(PKG, "csrc", "stream_ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libstream_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIPCC_FLAGS = [
@@ -27,13 +32,12 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(out: Optional[str] = None, defines: Optional[Dict[str, int]] = None, verbose: bool = False) -> str:
-    out = out or LIB
+def _compile(src: str, out: str, defines: Optional[Dict[str, int]], verbose: bool) -> str:
     cmd = [HIPCC, *HIPCC_FLAGS, "-I", INCLUDE]
     for k, v in (defines or {}).items():
         cmd.append(f"-D{k}={v}")
     tmp = out + ".tmp%d" % os.getpid()
-    cmd += ["-o", tmp, SRC]
+    cmd += ["-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -41,6 +45,21 @@ def build(out: Optional[str] = None, defines: Optional[Dict[str, int]] = None, v
     return out
 
 
+def build(out: Optional[str] = None, defines: Optional[Dict[str, int]] = None, verbose: bool = False) -> str:
+    """Build libar.so (or `out`) from csrc/ar.hip."""
+    return _compile(SRC, out or LIB, defines, verbose)
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """Build libstream_ceiling.so from csrc/stream_ceiling.hip."""
+    return _compile(CEILING_SRC, CEILING_LIB, None, verbose)
+
+
+def build_all(verbose: bool = False) -> None:
+    build(verbose=verbose)
+    build_ceiling(verbose=verbose)
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    build_all(verbose=True)
     sys.exit(0)
