@@ -2,12 +2,14 @@
  * stream_ceiling.h - C ABI of the streaming-ceiling kernels (libstream_ceiling.so).
  *
  * Measurement only, not part of the all-reduce path. One call reads n_in
- * buffers and writes n_out buffers of the same size once each, with the
- * simplest access pattern this GPU streams at: 16-byte non-temporal loads and
- * stores, 512 lanes x 2 packs per step, consecutive steps spread over the
- * grid. Timing it on the very buffers an all-reduce call uses (same sizes,
- * same addresses, same numbers of read and write streams) gives the practical
- * HBM ceiling of that call, next to the 8 TB/s peak.
+ * buffers and writes n_out buffers of the same size once each, with plain
+ * streaming code: 16-byte non-temporal loads and stores, a workgroup of
+ * `lanes` lanes covering lanes x packs 16-byte packs of every buffer per step,
+ * consecutive steps on consecutive workgroups. Timing it in each shape on the
+ * very buffers an all-reduce call uses (same sizes, same addresses, same
+ * numbers of read and write streams) and keeping the fastest gives the
+ * practical HBM ceiling of that call, next to the 8 TB/s peak. No one shape is
+ * fastest for every mix of streams.
  *
  * What it computes, per 16-byte pack i:
  *     x = in[0][i] ^ in[1][i] ^ ... ^ in[n_in-1][i]      (bitwise, as 4 x u32)
@@ -16,9 +18,10 @@
  * statement that consumes x.
  *
  * Arguments: `in` and `out` are host arrays of device pointers (the caller
- * owns every buffer); `bytes` is the size of each buffer. Outputs may not
- * overlap inputs or each other (not checked). The call is asynchronous on
- * `hip_stream` (NULL = default stream) of the current device.
+ * owns every buffer); `bytes` is the size of each buffer; `shape` is an
+ * SC_SHAPE_* value. Outputs may not overlap inputs or each other (not
+ * checked). The call is asynchronous on `hip_stream` (NULL = default stream)
+ * of the current device.
  *
  * Returns SC_OK, or a negative SC_ERR_* code without launching anything.
  */
@@ -35,16 +38,20 @@ extern "C" {
 #define SC_MAX_IN 12
 #define SC_MAX_OUT 2
 
+/* Workgroup shapes: lanes x packs per lane per step. */
+enum { SC_SHAPE_512x2 = 0, SC_SHAPE_256x4 = 1, SC_SHAPE_256x8 = 2, SC_SHAPE_128x8 = 3, SC_NUM_SHAPES = 4 };
+
 enum {
     SC_OK = 0,
     SC_ERR_COUNT = -1, /* n_in outside 1..SC_MAX_IN or n_out outside 0..SC_MAX_OUT    */
     SC_ERR_NULL = -2,  /* in or out array, or one of its first n pointers, is NULL     */
     SC_ERR_ALIGN = -3, /* a pointer not 16-byte aligned, or bytes not a multiple of 16 */
+    SC_ERR_SHAPE = -4, /* shape outside 0..SC_NUM_SHAPES-1                             */
     SC_ERR_HIP = -100  /* the launch failed                                             */
 };
 
 int32_t sc_stream(const void *const *in, int32_t n_in, void *const *out, int32_t n_out, size_t bytes,
-                  void *hip_stream);
+                  int32_t shape, void *hip_stream);
 
 #ifdef __cplusplus
 }

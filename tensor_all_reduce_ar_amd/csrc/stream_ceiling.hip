@@ -1,7 +1,8 @@
 // stream_ceiling.hip - streaming-ceiling kernels for gfx950 (measurement only;
 // C ABI in stream_ceiling.h). Each call reads NI buffers and writes NO buffers
-// of the same size once, in the access pattern of the all-reduce sum kernel
-// (512 lanes x 2 packs of 16 bytes per step, non-temporal), with no other work.
+// of the same size once, 16-byte non-temporal loads and stores, in one of a
+// few workgroup shapes (lanes x packs per lane per step), with no other work.
+// No single shape is fastest for every mix of streams, so a caller times each.
 
 #include <hip/hip_runtime.h>
 
@@ -13,8 +14,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
-constexpr int kUnroll = 2;
 constexpr unsigned kMaxGrid = 1u << 20;
 
 struct StreamArgs {
@@ -37,7 +36,10 @@ __device__ __forceinline__ void one_pack(const StreamArgs &a, size_t j)
         asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
 }
 
-template <int NI, int NO>
+// kThreads lanes x kUnroll packs per step; consecutive steps go to
+// consecutive workgroups; the packs after the last full step are done by the
+// last workgroup.
+template <int NI, int NO, int kThreads, int kUnroll>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a)
 {
     const size_t step = static_cast<size_t>(kThreads) * kUnroll;
@@ -67,31 +69,42 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a)
             one_pack<NI, NO>(a, j);
 }
 
-template <int NI, int NO>
+template <int NI, int NO, int T, int U>
 int32_t launch(const StreamArgs &a, hipStream_t stream)
 {
-    size_t blocks = a.npacks / (static_cast<size_t>(kThreads) * kUnroll);
+    size_t blocks = a.npacks / (static_cast<size_t>(T) * U);
     const unsigned grid = blocks < 1 ? 1u : blocks > kMaxGrid ? kMaxGrid : static_cast<unsigned>(blocks);
-    hipLaunchKernelGGL((stream_kernel<NI, NO>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((stream_kernel<NI, NO, T, U>), dim3(grid), dim3(T), 0, stream, a);
     return hipGetLastError() == hipSuccess ? SC_OK : SC_ERR_HIP;
 }
 
+template <int NI, int NO>
+int32_t by_shape(int shape, const StreamArgs &a, hipStream_t s)
+{
+    switch (shape) {
+    case SC_SHAPE_512x2: return launch<NI, NO, 512, 2>(a, s);
+    case SC_SHAPE_256x4: return launch<NI, NO, 256, 4>(a, s);
+    case SC_SHAPE_256x8: return launch<NI, NO, 256, 8>(a, s);
+    default: return launch<NI, NO, 128, 8>(a, s);
+    }
+}
+
 template <int NO>
-int32_t by_inputs(int n_in, const StreamArgs &a, hipStream_t s)
+int32_t by_inputs(int n_in, int shape, const StreamArgs &a, hipStream_t s)
 {
     switch (n_in) {
-    case 1: return launch<1, NO>(a, s);
-    case 2: return launch<2, NO>(a, s);
-    case 3: return launch<3, NO>(a, s);
-    case 4: return launch<4, NO>(a, s);
-    case 5: return launch<5, NO>(a, s);
-    case 6: return launch<6, NO>(a, s);
-    case 7: return launch<7, NO>(a, s);
-    case 8: return launch<8, NO>(a, s);
-    case 9: return launch<9, NO>(a, s);
-    case 10: return launch<10, NO>(a, s);
-    case 11: return launch<11, NO>(a, s);
-    default: return launch<12, NO>(a, s);
+    case 1: return by_shape<1, NO>(shape, a, s);
+    case 2: return by_shape<2, NO>(shape, a, s);
+    case 3: return by_shape<3, NO>(shape, a, s);
+    case 4: return by_shape<4, NO>(shape, a, s);
+    case 5: return by_shape<5, NO>(shape, a, s);
+    case 6: return by_shape<6, NO>(shape, a, s);
+    case 7: return by_shape<7, NO>(shape, a, s);
+    case 8: return by_shape<8, NO>(shape, a, s);
+    case 9: return by_shape<9, NO>(shape, a, s);
+    case 10: return by_shape<10, NO>(shape, a, s);
+    case 11: return by_shape<11, NO>(shape, a, s);
+    default: return by_shape<12, NO>(shape, a, s);
     }
 }
 
@@ -100,10 +113,12 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 extern "C" int32_t sc_stream(const void *const *in, int32_t n_in, void *const *out, int32_t n_out, size_t bytes,
-                             void *hip_stream)
+                             int32_t shape, void *hip_stream)
 {
     if (n_in < 1 || n_in > SC_MAX_IN || n_out < 0 || n_out > SC_MAX_OUT)
         return SC_ERR_COUNT;
+    if (shape < 0 || shape >= SC_NUM_SHAPES)
+        return SC_ERR_SHAPE;
     if (!in || (n_out > 0 && !out))
         return SC_ERR_NULL;
     if (bytes % 16 != 0)
@@ -128,8 +143,8 @@ extern "C" int32_t sc_stream(const void *const *in, int32_t n_in, void *const *o
         return SC_OK;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     switch (n_out) {
-    case 0: return by_inputs<0>(n_in, a, s);
-    case 1: return by_inputs<1>(n_in, a, s);
-    default: return by_inputs<2>(n_in, a, s);
+    case 0: return by_inputs<0>(n_in, shape, a, s);
+    case 1: return by_inputs<1>(n_in, shape, a, s);
+    default: return by_inputs<2>(n_in, shape, a, s);
     }
 }

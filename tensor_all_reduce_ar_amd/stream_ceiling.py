@@ -1,9 +1,10 @@
 """ctypes binding of ``libstream_ceiling.so`` (C ABI in include/stream_ceiling.h).
 
-Measurement only: ``sc_stream(inputs, outputs)`` reads every input tensor and
-writes every output tensor once (outputs = bitwise XOR of the inputs), with
-the plainest streaming pattern, so that timing it on an all-reduce call's own
-buffers gives that call's practical HBM ceiling.
+Measurement only: ``sc_stream(inputs, outputs, shape)`` reads every input
+tensor and writes every output tensor once (outputs = bitwise XOR of the
+inputs) with plain streaming code in one of SHAPES, so that timing it on an
+all-reduce call's own buffers, in every shape, gives that call's practical HBM
+ceiling.
 """
 from __future__ import annotations
 
@@ -14,6 +15,8 @@ from typing import Optional, Sequence
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstream_ceiling.so")
 SC_MAX_IN, SC_MAX_OUT = 12, 2
 SC_OK = 0
+# SC_SHAPE_* of include/stream_ceiling.h: lanes x packs per lane per step
+SHAPES = {0: "512x2", 1: "256x4", 2: "256x8", 3: "128x8"}
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -27,20 +30,20 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is missing: build it with `python -m tensor_all_reduce_ar_amd.build`")
     L = ctypes.CDLL(path)
     L.sc_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
-                            ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p]
+                            ctypes.c_int32, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
     L.sc_stream.restype = ctypes.c_int32
     _lib = L
     return L
 
 
-def sc_stream_raw(inputs: Sequence[int], outputs: Sequence[int], nbytes: int, stream: int = 0) -> int:
+def sc_stream_raw(inputs: Sequence[int], outputs: Sequence[int], nbytes: int, shape: int = 0, stream: int = 0) -> int:
     """sc_stream on raw device addresses; returns the status."""
     ins = (ctypes.c_void_p * max(1, len(inputs)))(*inputs)
     outs = (ctypes.c_void_p * max(1, len(outputs)))(*outputs) if outputs else None
-    return load().sc_stream(ins, len(inputs), outs, len(outputs), nbytes, ctypes.c_void_p(stream))
+    return load().sc_stream(ins, len(inputs), outs, len(outputs), nbytes, shape, ctypes.c_void_p(stream))
 
 
-def sc_stream(inputs: Sequence, outputs: Sequence, stream=None) -> None:
+def sc_stream(inputs: Sequence, outputs: Sequence, shape: int = 0, stream=None) -> None:
     """Read every tensor of `inputs` and write every tensor of `outputs` once
     (contiguous device tensors of one byte size, a multiple of 16)."""
     import torch
@@ -49,6 +52,6 @@ def sc_stream(inputs: Sequence, outputs: Sequence, stream=None) -> None:
         if not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() != nbytes:
             raise ValueError("sc_stream needs contiguous device tensors of one byte size")
     h = int((stream or torch.cuda.current_stream()).cuda_stream)
-    st = sc_stream_raw([t.data_ptr() for t in inputs], [t.data_ptr() for t in outputs], nbytes, h)
+    st = sc_stream_raw([t.data_ptr() for t in inputs], [t.data_ptr() for t in outputs], nbytes, shape, h)
     if st != SC_OK:
         raise RuntimeError(f"sc_stream failed with status {st}")

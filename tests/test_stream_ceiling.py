@@ -33,8 +33,13 @@ def test_negative_counts():
     import ctypes
     ins = (ctypes.c_void_p * 2)(A, A + 4096)
     outs = (ctypes.c_void_p * 1)(A + 8192)
-    assert sc.load().sc_stream(ins, 2, outs, -1, 1024, None) == -1
-    assert sc.load().sc_stream(ins, -2, outs, 1, 1024, None) == -1
+    assert sc.load().sc_stream(ins, 2, outs, -1, 1024, 0, None) == -1
+    assert sc.load().sc_stream(ins, -2, outs, 1, 1024, 0, None) == -1
+
+
+@pytest.mark.parametrize("shape", [-1, 4])
+def test_bad_shape(shape):
+    assert sc.sc_stream_raw([A], [A + 4096], 1024, shape) == -4
 
 
 def test_null_and_alignment():
@@ -50,21 +55,22 @@ def test_zero_bytes_is_a_noop_without_any_hip_call():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("shape", sorted(sc.SHAPES))
 @pytest.mark.parametrize("n_in,n_out", [(1, 0), (1, 1), (4, 1), (9, 2), (12, 2)])
-def test_outputs_are_the_xor_of_the_inputs(n_in, n_out):
+def test_outputs_are_the_xor_of_the_inputs(n_in, n_out, shape):
     import torch
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
     rng = np.random.default_rng(n_in * 10 + n_out)
-    for packs in (1, 1023, 1024, 3 * 1024 + 5, 100003):
-        print(f"[stream] n_in={n_in} n_out={n_out} packs={packs}", flush=True)
+    for packs in (1, 1023, 1024, 2048, 3 * 2048 + 5, 100003):
+        print(f"[stream] n_in={n_in} n_out={n_out} shape={shape} packs={packs}", flush=True)
         host = [rng.integers(0, 2 ** 32, size=4 * packs, dtype=np.uint32) for _ in range(n_in)]
         ins = [torch.from_numpy(h.view(np.int32)).cuda() for h in host]
         guard = 1024
         raw = [torch.full((4 * packs + 2 * guard,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
                for _ in range(n_out)]
         outs = [r[guard:guard + 4 * packs] for r in raw]
-        sc.sc_stream(ins, outs)
+        sc.sc_stream(ins, outs, shape)
         torch.cuda.synchronize()
         want = np.bitwise_xor.reduce(np.stack(host), axis=0)
         for r in raw:
