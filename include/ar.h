@@ -44,10 +44,11 @@
  *
  * Ownership and execution: the caller owns every buffer (device memory, e.g.
  * from torch). The library allocates no device memory, keeps no state between
- * calls that affects results (it caches the device's CU count and kernel
- * occupancies) and needs no workspace. Calls are asynchronous on the caller's HIP stream
- * (NULL = the default stream): outputs are valid once the stream has been
- * synchronized. Calls are re-entrant and thread-safe.
+ * calls that affects results (it caches each device's CU count and kernel
+ * occupancies, by device index) and needs no workspace. Calls are
+ * asynchronous on the caller's HIP stream (NULL = the default stream):
+ * outputs are valid once the stream has been synchronized. Calls are
+ * re-entrant and thread-safe.
  *
  * Errors: every entry point returns AR_OK (0) or a negative AR_ERR_* code and
  * never throws. On a validation error nothing is launched and no output is

@@ -718,39 +718,52 @@ int32_t launch_sum(const ar_params_t *p, hipStream_t stream, bool vec)
     return check_launch("ar_sum launch");
 }
 
-// Compute units of the current device (cached per device).
-int device_cus()
+// Launch-shape queries are cached per device index below kCachedDevices (a
+// larger index queries every time). 0 in a cache slot means not yet known.
+constexpr int kCachedDevices = 16;
+using OccCache = std::atomic<int>[kCachedDevices][kFusedMaxThreads / kWave + 1];
+
+int current_device()
 {
-    static std::atomic<int> cache[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
-        return 256;
-    if (dev < 64) {
+    return hipGetDevice(&dev) == hipSuccess && dev >= 0 ? dev : -1;
+}
+
+// Compute units of device `dev` (256, the MI355X count, if it cannot be queried).
+int device_cus(int dev)
+{
+    static std::atomic<int> cache[kCachedDevices];
+    const bool cached = dev >= 0 && dev < kCachedDevices;
+    if (cached) {
         int c = cache[dev].load(std::memory_order_relaxed);
         if (c > 0)
             return c;
     }
     int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (dev < 64)
+    if (cached)
         cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
-// Resident workgroups per CU of `kernel` at `threads` per workgroup (cached
-// per kernel instantiation and workgroup size).
+// Resident workgroups per CU of `kernel` at `threads` per workgroup on device
+// `dev` (cache: one per kernel instantiation, slots per device and size).
 template <class K>
-int resident_per_cu(K kernel, int threads, std::atomic<int> (&cache)[kFusedMaxThreads / kWave + 1])
+int resident_per_cu(K kernel, int threads, int dev, OccCache &cache)
 {
     const int slot = threads / kWave;
-    int c = cache[slot].load(std::memory_order_relaxed);
-    if (c > 0)
-        return c;
+    const bool cached = dev >= 0 && dev < kCachedDevices;
+    if (cached) {
+        int c = cache[dev][slot].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0)
         n = 1;
-    cache[slot].store(n, std::memory_order_relaxed);
+    if (cached)
+        cache[dev][slot].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -758,11 +771,11 @@ int resident_per_cu(K kernel, int threads, std::atomic<int> (&cache)[kFusedMaxTh
 // workgroups per CU) that loop over the rows: no second dispatch round, whose
 // refill leaves CUs idle.
 template <class E, int R, int PPT, int BOUND>
-void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int cus, hipStream_t stream)
+void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
 {
-    static std::atomic<int> occ[kFusedMaxThreads / kWave + 1];
+    static OccCache occ;
     const size_t resident =
-        static_cast<size_t>(cus) * resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT, BOUND>, threads, occ);
+        static_cast<size_t>(cus) * resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT, BOUND>, threads, dev, occ);
     if (grid > resident)
         grid = static_cast<unsigned>(resident);
     hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT, BOUND>), dim3(grid), dim3(threads), 0, stream, a);
@@ -784,11 +797,12 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
     a.rows = p->elts_total / static_cast<size_t>(f.hidden_size);
     a.eps = f.eps;
     const unsigned grid = clamp_grid(a.rows);
-    int cus = 0;
+    int dev = -1, cus = 0;
     FusedGeometry g{0, 0, 0};
     if (vec) {
         a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
-        cus = device_cus();
+        dev = current_device();
+        cus = device_cus(dev);
         g = fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus));
     }
     if (vec && g.ppt == 0) {
@@ -803,20 +817,20 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
         const int t = g.threads;
         if (g.bound == kFusedMaxThreads) {
             switch (g.ppt) {
-            case 1: launch_fused_pack<E, R, 1, kFusedMaxThreads>(a, grid, t, cus, stream); break;
-            case 2: launch_fused_pack<E, R, 2, kFusedMaxThreads>(a, grid, t, cus, stream); break;
+            case 1: launch_fused_pack<E, R, 1, kFusedMaxThreads>(a, grid, t, dev, cus, stream); break;
+            case 2: launch_fused_pack<E, R, 2, kFusedMaxThreads>(a, grid, t, dev, cus, stream); break;
             default: return AR_ERR_SHAPE;  // unreachable: the latency layout yields 1..kLatencyMaxPPT
             }
         } else {
             switch (g.ppt) {
-            case 1: launch_fused_pack<E, R, 1, 512>(a, grid, t, cus, stream); break;
-            case 2: launch_fused_pack<E, R, 2, 512>(a, grid, t, cus, stream); break;
-            case 3: launch_fused_pack<E, R, 3, 256>(a, grid, t, cus, stream); break;
-            case 4: launch_fused_pack<E, R, 4, 256>(a, grid, t, cus, stream); break;
-            case 5: launch_fused_pack<E, R, 5, 256>(a, grid, t, cus, stream); break;
-            case 6: launch_fused_pack<E, R, 6, 256>(a, grid, t, cus, stream); break;
-            case 7: launch_fused_pack<E, R, 7, 256>(a, grid, t, cus, stream); break;
-            case 8: launch_fused_pack<E, R, 8, 256>(a, grid, t, cus, stream); break;
+            case 1: launch_fused_pack<E, R, 1, 512>(a, grid, t, dev, cus, stream); break;
+            case 2: launch_fused_pack<E, R, 2, 512>(a, grid, t, dev, cus, stream); break;
+            case 3: launch_fused_pack<E, R, 3, 256>(a, grid, t, dev, cus, stream); break;
+            case 4: launch_fused_pack<E, R, 4, 256>(a, grid, t, dev, cus, stream); break;
+            case 5: launch_fused_pack<E, R, 5, 256>(a, grid, t, dev, cus, stream); break;
+            case 6: launch_fused_pack<E, R, 6, 256>(a, grid, t, dev, cus, stream); break;
+            case 7: launch_fused_pack<E, R, 7, 256>(a, grid, t, dev, cus, stream); break;
+            case 8: launch_fused_pack<E, R, 8, 256>(a, grid, t, dev, cus, stream); break;
             default: return AR_ERR_SHAPE;  // unreachable: fused_geometry yields 0..kMaxPPT
             }
         }
