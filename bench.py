@@ -115,18 +115,42 @@ def dev(torch, a, dtype):
     return torch.from_numpy(a).cuda()
 
 
-def bench_fused(torch, ar, w, args, stream):
+def slab_copies(torch, ar, parts):
+    """Copies of the device partials in one allocation at the slot offsets of
+    ar_partials_layout; returns (allocation, views)."""
+    code = {torch.float32: ar.AR_FP32, torch.float16: ar.AR_FP16, torch.bfloat16: ar.AR_BF16}[parts[0].dtype]
+    n, size = parts[0].numel(), parts[0].element_size()
+    st, offs, total = ar.ar_partials_layout(n, code, len(parts))
+    assert st == ar.AR_OK, ar.ar_status_string(st)
+    base = torch.empty(total, dtype=torch.uint8, device="cuda")
+    views = []
+    for off, p in zip(offs, parts):
+        v = base[off:off + n * size].view(p.dtype)
+        v.copy_(p)
+        views.append(v)
+    return base, views
+
+
+def bench_fused(torch, ar, w, args, stream, layout="separate"):
+    """layout: "separate" (one allocation per partial) or "slab" (the partials
+    of a set in one allocation at ar_partials_layout's slots)."""
     nb = w.algorithmic_bytes()
     nsets = rotation_sets(nb, 2 * w.n * w.itemsize)
     base = [dev(torch, p, w.dtype) for p in w.partials]
     res0 = dev(torch, w.residual, w.dtype)
     weight = dev(torch, w.weight, w.dtype)
     bias = dev(torch, w.bias, w.dtype) if w.bias is not None else None
-    sets = []
+    sets, keep = [], []
     for k in range(nsets):
-        parts = base if k == 0 else [p.clone() for p in base]
+        if layout == "slab":
+            slab, parts = slab_copies(torch, ar, base)
+            keep.append(slab)
+        else:
+            parts = base if k == 0 else [p.clone() for p in base]
         res = res0 if k == 0 else res0.clone()
         sets.append((parts, res, torch.empty_like(res0), torch.empty_like(res0)))
+    if layout == "slab":
+        del base
 
     def launch(k):
         parts, res, out, inter = sets[k]
@@ -510,6 +534,21 @@ def main():
         print(f"[bench] two-shot share: {sl['ms_step'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
 
     if not args.no_next:
+        sl = bench_fused(torch, ar, w, args, stream, layout="slab")
+        sl_gbps = sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9
+        result["fused_partials_in_layout"] = {
+            "what": "the same fused workload with each set's partials in one allocation at the slots of "
+                    "ar_partials_layout (4 KiB more stagger per partial)",
+            "us_per_call": round(sl["ms_step"] * 1e3, 2), "gbps": round(sl_gbps, 1),
+            "frac": round(sl_gbps / HBM_PEAK_GBPS, 4),
+            "stream_ceiling_same_buffers": sl["ceil"],
+            "frac_of_stream_ceiling": round(sl_gbps / sl["ceil"]["gbps"], 4),
+            "gpu_matches_separate_layout": bool(np.array_equal(sl["out_bits"], gpu_out) and
+                                                np.array_equal(sl["inter_bits"], gpu_inter)),
+        }
+        print(f"[bench] fused, partials in ar_partials_layout slots: {sl['ms_step'] * 1e3:.1f} us/call "
+              f"({sl_gbps:.0f} GB/s)", file=sys.stderr, flush=True)
+        del sl
         mw = inputs.make(inputs.fused_fp16_r2_5120_name(4096))
         m = bench_fused(torch, ar, mw, args, stream)
         m_gbps = m["bytes"] / (m["ms_step"] * 1e-3) / 1e9

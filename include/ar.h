@@ -191,6 +191,31 @@ int32_t ar_configuration_supported(const ar_params_t *p, int32_t fusion_op);
  * getWorkspaceSize on the "All Reduce Plugin" page). p may be NULL. */
 size_t ar_workspace_size(const ar_params_t *p);
 
+/* Byte distance added between consecutive partial slots by ar_partials_layout,
+ * and the alignment of every slot. */
+#define AR_SLOT_STAGGER_BYTES 4096
+#define AR_SLOT_ALIGN_BYTES 256
+
+/*
+ * Layout of the R partials in one caller-owned allocation (the one-GPU
+ * counterpart of the comm-buffer workspace that CustomAllReduceHelper sizes
+ * and allocates in "allreduce.d2"). Slot r starts at
+ *     slot_offsets[r] = r * (round_up(elts_total * sizeof(T), AR_SLOT_ALIGN_BYTES)
+ *                            + AR_SLOT_STAGGER_BYTES)
+ * bytes from the base, and *total_bytes is the size to allocate (R slots).
+ * Separate allocations of a large power-of-two size place element i of every
+ * partial at the same offset within the same HBM interleave pattern; the
+ * stagger moves each partial by 4 KiB more than the previous one, which the
+ * fused kernel reads faster (about 5 % on MI355X at 8 bf16 partials of
+ * [2048, 8192]). Any layout stays valid for every entry point; this one is a
+ * recommendation. The base must be AR_SLOT_ALIGN_BYTES-aligned (hipMalloc and
+ * torch allocations are) so that every slot takes the 16-byte vector path.
+ * slot_offsets has room for `ranks` entries. Makes no HIP call.
+ * Returns AR_OK, AR_ERR_RANKS, AR_ERR_DTYPE or AR_ERR_NULL.
+ */
+int32_t ar_partials_layout(size_t elts_total, int32_t dtype, int32_t ranks, size_t *slot_offsets,
+                           size_t *total_bytes);
+
 /* Static, never-NULL description of a status code (unknown codes included). */
 const char *ar_status_string(int32_t status);
 

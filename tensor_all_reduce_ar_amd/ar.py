@@ -15,7 +15,7 @@ Entry points, same names as the C ABI:
                                                           one share of a two-shot split
   ar_slice_range(params, fusion_op, slice_index, num_slices)
   ar_configuration_supported(params, fusion_op), ar_workspace_size(params),
-  ar_status_string(code), ar_last_hip_error()
+  ar_partials_layout(elts_total, dtype, ranks), ar_status_string(code), ar_last_hip_error()
 plus ``Params`` / ``make_params``, ``call`` and ``call_slice`` for raw-pointer use.
 """
 from __future__ import annotations
@@ -32,11 +32,12 @@ AR_FUSION_NONE, AR_FUSION_RESIDUAL_RMS_NORM = 0, 1
 AR_OK = 0
 AR_ERR_NULL, AR_ERR_RANKS, AR_ERR_DTYPE, AR_ERR_SHAPE = -1, -2, -3, -4
 AR_ERR_EPS, AR_ERR_ALIAS, AR_ERR_ALIGN, AR_ERR_SLICE, AR_ERR_HIP = -5, -6, -7, -8, -100
+AR_SLOT_STAGGER_BYTES, AR_SLOT_ALIGN_BYTES = 4096, 256
 
 # Every function include/ar.h declares.
 EXPORTS = ("ar_sum", "ar_residual_rmsnorm", "ar_rmsnorm", "ar_sum_slice", "ar_residual_rmsnorm_slice",
-           "ar_slice_range", "ar_configuration_supported", "ar_workspace_size", "ar_status_string",
-           "ar_last_hip_error")
+           "ar_slice_range", "ar_configuration_supported", "ar_workspace_size", "ar_partials_layout",
+           "ar_status_string", "ar_last_hip_error")
 
 
 class FusionParams(ctypes.Structure):
@@ -100,6 +101,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.ar_configuration_supported.restype = ctypes.c_int32
     L.ar_workspace_size.argtypes = [P]
     L.ar_workspace_size.restype = ctypes.c_size_t
+    L.ar_partials_layout.argtypes = [ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t),
+                                     ctypes.POINTER(ctypes.c_size_t)]
+    L.ar_partials_layout.restype = ctypes.c_int32
     L.ar_status_string.argtypes = [ctypes.c_int32]
     L.ar_status_string.restype = ctypes.c_char_p
     L.ar_last_hip_error.argtypes = []
@@ -161,6 +165,15 @@ def ar_configuration_supported(params: Params, fusion_op: int) -> int:
 
 def ar_workspace_size(params: Optional[Params] = None) -> int:
     return load().ar_workspace_size(ctypes.byref(params) if params is not None else None)
+
+
+def ar_partials_layout(elts_total: int, dtype: int, ranks: int):
+    """(status, slot byte offsets, total bytes) of the recommended one-allocation
+    layout of `ranks` partials of `elts_total` elements of type `dtype`."""
+    offs = (ctypes.c_size_t * max(1, ranks))()
+    total = ctypes.c_size_t(0)
+    st = load().ar_partials_layout(elts_total, dtype, ranks, offs if ranks > 0 else None, ctypes.byref(total))
+    return st, [offs[r] for r in range(max(0, ranks))] if st == AR_OK else [], total.value
 
 
 # ------------------------------------------------------------ torch front end

@@ -1051,6 +1051,22 @@ size_t ar_workspace_size(const ar_params_t *p)
     return 0;
 }
 
+int32_t ar_partials_layout(size_t elts_total, int32_t dtype, int32_t ranks, size_t *slot_offsets, size_t *total_bytes)
+{
+    if (dtype != AR_FP32 && dtype != AR_FP16 && dtype != AR_BF16)
+        return AR_ERR_DTYPE;
+    if (ranks < 1 || ranks > AR_MAX_RANKS)
+        return AR_ERR_RANKS;
+    if (!slot_offsets || !total_bytes)
+        return AR_ERR_NULL;
+    const size_t a = AR_SLOT_ALIGN_BYTES;
+    const size_t stride = (elts_total * elem_size(dtype) + a - 1) / a * a + AR_SLOT_STAGGER_BYTES;
+    for (int r = 0; r < ranks; ++r)
+        slot_offsets[r] = static_cast<size_t>(r) * stride;
+    *total_bytes = static_cast<size_t>(ranks) * stride;
+    return AR_OK;
+}
+
 const char *ar_status_string(int32_t status)
 {
     switch (status) {

@@ -58,6 +58,7 @@ int main(void) {
   printf("enum.AR_ERR_EPS %d\nenum.AR_ERR_ALIAS %d\nenum.AR_ERR_ALIGN %d\nenum.AR_ERR_HIP %d\n",
          AR_ERR_EPS, AR_ERR_ALIAS, AR_ERR_ALIGN, AR_ERR_HIP);
   printf("enum.AR_ERR_SLICE %d\n", AR_ERR_SLICE);
+  printf("enum.AR_SLOT_STAGGER_BYTES %d\nenum.AR_SLOT_ALIGN_BYTES %d\n", AR_SLOT_STAGGER_BYTES, AR_SLOT_ALIGN_BYTES);
   return 0;
 }
 ''')
@@ -78,7 +79,8 @@ def test_ctypes_mirrors_match_the_header(tmp_path):
         assert c[f"ar_fusion_params_t.{f}"] == getattr(ar.FusionParams, f).offset, f
     for name in ("AR_MAX_RANKS", "AR_FP32", "AR_FP16", "AR_BF16", "AR_FUSION_NONE", "AR_FUSION_RESIDUAL_RMS_NORM",
                  "AR_OK", "AR_ERR_NULL", "AR_ERR_RANKS", "AR_ERR_DTYPE", "AR_ERR_SHAPE", "AR_ERR_EPS",
-                 "AR_ERR_ALIAS", "AR_ERR_ALIGN", "AR_ERR_SLICE", "AR_ERR_HIP"):
+                 "AR_ERR_ALIAS", "AR_ERR_ALIGN", "AR_ERR_SLICE", "AR_ERR_HIP", "AR_SLOT_STAGGER_BYTES",
+                 "AR_SLOT_ALIGN_BYTES"):
         assert c[f"enum.{name}"] == getattr(ar, name), name
 
 
@@ -211,6 +213,32 @@ def test_workspace_and_status_strings():
         s = ar.ar_status_string(code)
         assert isinstance(s, str) and s
     assert ar.ar_status_string(ar.AR_ERR_ALIAS).startswith("AR_ERR_ALIAS")
+
+
+@pytest.mark.parametrize("dtype,size", [(ar.AR_FP32, 4), (ar.AR_FP16, 2), (ar.AR_BF16, 2)])
+@pytest.mark.parametrize("n", [0, 1, 100, 4096, 2048 * 8192, (1 << 31) + 1003])
+def test_partials_layout(dtype, size, n):
+    """Slots: consecutive, in order, each 256-byte aligned, at least the
+    partial's bytes apart, and 4 KiB further apart than the rounded size."""
+    for ranks in range(1, 9):
+        st, offs, total = ar.ar_partials_layout(n, dtype, ranks)
+        assert st == ar.AR_OK and len(offs) == ranks
+        stride = -(-n * size // 256) * 256 + 4096
+        assert offs == [r * stride for r in range(ranks)]
+        assert total == ranks * stride
+        for r in range(ranks):
+            assert offs[r] % 256 == 0
+            assert offs[r] + n * size <= (offs[r + 1] if r + 1 < ranks else total)
+
+
+def test_partials_layout_errors():
+    assert ar.ar_partials_layout(100, 7, 2)[0] == ar.AR_ERR_DTYPE
+    assert ar.ar_partials_layout(100, ar.AR_FP16, 0)[0] == ar.AR_ERR_RANKS
+    assert ar.ar_partials_layout(100, ar.AR_FP16, 9)[0] == ar.AR_ERR_RANKS
+    total = ctypes.c_size_t(0)
+    assert ar.load().ar_partials_layout(100, ar.AR_FP16, 2, None, ctypes.byref(total)) == ar.AR_ERR_NULL
+    offs = (ctypes.c_size_t * 2)()
+    assert ar.load().ar_partials_layout(100, ar.AR_FP16, 2, offs, None) == ar.AR_ERR_NULL
 
 
 def test_unknown_fusion_op_rejected():

@@ -10,6 +10,10 @@ Two-shot split ("allreduce.d2" twoShotAllReduceKernel; "type.d2"
 elts_per_rank): each slice call computes one rank's share in place in the full
 output; all slices together must equal the oracle's full result, and one
 slice must write exactly its range.
+
+Partials layout (ar_partials_layout, the one-GPU counterpart of the comm-buffer
+workspace of "allreduce.d2" CustomAllReduceHelper): partials placed in one
+allocation at the recommended staggered slots give the oracle's results.
 """
 import numpy as np
 import pytest
@@ -19,7 +23,7 @@ import oracle
 import tensor_all_reduce_ar_amd as ar
 from tensor_all_reduce_ar_amd import inputs
 
-from gpu_util import (Guarded, assert_bitexact, assert_output_close, bits, dev, empty_host, host_bits, note)
+from gpu_util import (Guarded, assert_bitexact, assert_output_close, bits, dev, empty_host, host_bits, note, slab)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -161,3 +165,37 @@ def test_two_shot_split_at_the_large_shapes():
         ar.ar_sum_slice(sp, so, k, 4)
     torch.cuda.synchronize()
     assert_bitexact(host_bits(so), bits(oracle_sum(s)), s.dtype, "large sum, 4 slices")
+
+
+# ------------------------------------------------------- partials layout
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ranks", [1, 2, 8])
+def test_ops_on_partials_in_the_recommended_layout(dtype, ranks):
+    note(f"[next] slab layout {dtype} R={ranks}")
+    w = inputs.random_fused(dtype, ranks, 37, 4096, 1600 + ranks)
+    base, parts = slab(w.partials, dtype)
+    out, inter = Guarded(w.n, dtype), Guarded(w.n, dtype)
+    ar.ar_residual_rmsnorm(parts, dev(w.weight, dtype), w.eps, out.t, inter.t, bias=dev(w.bias, dtype),
+                           residual=dev(w.residual, dtype))
+    s_out = Guarded(w.n, dtype)
+    ar.ar_sum(parts, s_out.t)
+    torch.cuda.synchronize()
+    for g in (out, inter, s_out):
+        g.check_guards()
+    ref_out, ref_inter = oracle_fused(w)
+    assert_bitexact(host_bits(inter.t), ref_inter, dtype, "slab layout intermediate")
+    assert_output_close(host_bits(out.t), ref_out, dtype, "slab layout output")
+    assert_bitexact(host_bits(s_out.t), bits(oracle_sum(w)), dtype, "slab layout sum")
+    del base
+
+
+def test_large_fused_workload_in_the_recommended_layout():
+    w = inputs.make(inputs.FUSED_BF16_R8_2048x8192)
+    base, parts = slab(w.partials, w.dtype)
+    out, inter = torch.empty_like(parts[0]), torch.empty_like(parts[0])
+    ar.ar_residual_rmsnorm(parts, dev(w.weight, w.dtype), w.eps, out, inter, residual=dev(w.residual, w.dtype))
+    torch.cuda.synchronize()
+    ref_out, ref_inter = oracle_fused(w)
+    assert_bitexact(host_bits(inter), ref_inter, w.dtype, "large fused, slab layout, intermediate")
+    assert_output_close(host_bits(out), ref_out, w.dtype, "large fused, slab layout, output")
+    del base
