@@ -81,6 +81,8 @@ constexpr int kSumThreads = AR_SUM_THREADS;
 constexpr int kMaxPPT = 8;
 constexpr int kFusedMaxThreads = 1024;
 constexpr int kLatencyMaxPPT = 2;
+constexpr int kFullMaxPPT = 5;   // full-row variant: slots per lane, at most
+constexpr int kFullLanes = 128;  // full-row variant: workgroup size
 constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
 constexpr int kElemThreads = 256;       // element-wise kernels
 constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
@@ -388,12 +390,31 @@ __device__ __forceinline__ u32x4 normed_pack(u32x4 sp, float rstd, u32x4 wp)
     return E::narrow(o);
 }
 
+// The R partial packs and the residual pack (zero if there is none) at pack
+// index j.
+template <int R>
+__device__ __forceinline__ void load_slot(const FusedArgs &a, size_t j, u32x4 (&v)[R], u32x4 &rq)
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        v[r] = ld16(static_cast<const u32x4 *>(a.in[r]) + j);
+    rq = a.residual ? ld16(static_cast<const u32x4 *>(a.residual) + j) : u32x4{0, 0, 0, 0};
+}
+
 // Fused op, one row per workgroup at a time (the resident grid loops over the
 // rows), for rows of up to kMaxPPT * 256 packs. Lane l holds packs l, l+T, ...,
 // l+(PPT-1)T of the row (T = workgroup size), so each load instruction of a
 // wave covers 1 KiB contiguous. The rounded S stays in registers as packs
 // (4 VGPRs per pack) and the weight packs are loaded before the barrier.
-template <class E, int R, int PPT, int BOUND>
+// FULL: the row fills every slot of every lane (ppr == PPT * T). The slots
+// then need no bounds test and are software-pipelined two deep: slot p+1's
+// loads are issued before slot p's sums, and a compiler fence after each slot
+// keeps later slots' loads from being hoisted further (which would hold every
+// slot's loads in registers). The S stores wait until the last slot: a store
+// between two slots would order the next slot's loads after it (S may be a
+// partial or the residual, so the compiler must assume they overlap). Every
+// element is still read before its own S is written.
+template <class E, int R, int PPT, int BOUND, bool FULL>
 __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
 {
     __shared__ float part[BOUND / kWave];
@@ -405,6 +426,24 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
         const size_t row0 = row * static_cast<size_t>(a.ppr);
         u32x4 sp[PPT], w[PPT];
         float ss = 0.0f;
+        if (FULL) {
+            u32x4 v[2][R], rq[2];
+            load_slot<R>(a, row0 + threadIdx.x, v[0], rq[0]);
+#pragma unroll
+            for (int p = 0; p < PPT; ++p) {
+                const int j = threadIdx.x + p * T;
+                if (p + 1 < PPT)
+                    load_slot<R>(a, row0 + j + T, v[(p + 1) & 1], rq[(p + 1) & 1]);
+                const u32x4 bq = bias ? bias[j] : u32x4{0, 0, 0, 0};
+                w[p] = weight[j];
+                sp[p] = fused_pre_norm<E, R>(v[p & 1], bias != nullptr, bq, a.residual != nullptr, rq[p & 1]);
+                ss += sum_squares<E>(sp[p]);
+                asm volatile("" ::: "memory");
+            }
+#pragma unroll
+            for (int p = 0; p < PPT; ++p)
+                st16(static_cast<u32x4 *>(a.inter) + row0 + threadIdx.x + p * T, sp[p]);
+        } else {
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int j = threadIdx.x + p * T;
@@ -424,13 +463,14 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
                 ss += sum_squares<E>(sp[p]);
             }
         }
+        }
 
         const float rstd = rms_scale(block_sum(ss, part), a.hidden, a.eps);
 
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int j = threadIdx.x + p * T;
-            if (j < a.ppr)
+            if (FULL || j < a.ppr)
                 st16(static_cast<u32x4 *>(a.out) + row0 + j, normed_pack<E>(sp[p], rstd, w[p]));
         }
         __syncthreads();  // `part` is rewritten by the next row
@@ -628,11 +668,18 @@ struct FusedGeometry {
 };
 
 // Throughput layout: 1 pack per lane up to 512 packs, 2 up to 1024, then
-// ceil(ppr / 256) up to kMaxPPT. Latency layout (`few_rows`, rows of more than
-// 512 packs): ceil(ppr / 1024) packs per lane, up to kLatencyMaxPPT.
+// ceil(ppr / 256) up to kMaxPPT. Where that workgroup would hold 3, 5, 6 or 7
+// waves (so a CU's 4 SIMDs get unequal shares) and the row is 3 or 5 blocks of
+// 128 packs, it takes 128 lanes with 3 or 5 packs each instead: measured
+// 2-8 % faster on rows of 384 and 640 packs (for 16-bit types, hidden 3072
+// and 5120), where 7 blocks (896 packs) measured slower. Latency layout
+// (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024) packs per lane,
+// up to kLatencyMaxPPT.
 FusedGeometry fused_geometry(int ppr, bool few_rows)
 {
     int k, bound;
+    if (!few_rows && (ppr == 3 * kFullLanes || ppr == 5 * kFullLanes))
+        return FusedGeometry{ppr / kFullLanes, kFullLanes, 256};
     if (few_rows && ppr > 512 && ppr <= kLatencyMaxPPT * kFusedMaxThreads) {
         k = (ppr + kFusedMaxThreads - 1) / kFusedMaxThreads;
         bound = kFusedMaxThreads;
@@ -770,15 +817,32 @@ int resident_per_cu(K kernel, int threads, int dev, OccCache &cache)
 // The register-row kernel runs as one resident wave of workgroups (CUs x
 // workgroups per CU) that loop over the rows: no second dispatch round, whose
 // refill leaves CUs idle.
+template <class E, int R, int PPT, int BOUND, bool FULL>
+void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
+{
+    static OccCache occ;
+    const size_t resident = static_cast<size_t>(cus) *
+                            resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, FULL>, threads, dev, occ);
+    if (grid > resident)
+        grid = static_cast<unsigned>(resident);
+    hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, FULL>), dim3(grid), dim3(threads), 0, stream, a);
+}
+
+// The pipelined full-row variant runs where it was measured faster: the
+// 128-lane layout (3 or 5 packs per lane, the rows of 384 and 640 packs), 2-9 %
+// over the plain slots. With one or two slots on 512 lanes (rows of 512 and
+// 1024 packs) it was as fast or up to 7 % slower: two slots' loads in flight
+// per lane cost more there than the overlap gains.
 template <class E, int R, int PPT, int BOUND>
 void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
 {
-    static OccCache occ;
-    const size_t resident =
-        static_cast<size_t>(cus) * resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT, BOUND>, threads, dev, occ);
-    if (grid > resident)
-        grid = static_cast<unsigned>(resident);
-    hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT, BOUND>), dim3(grid), dim3(threads), 0, stream, a);
+    if constexpr (PPT >= 3 && PPT <= kFullMaxPPT) {
+        if (threads == kFullLanes && a.ppr == PPT * threads) {
+            launch_fused_pack_as<E, R, PPT, BOUND, true>(a, grid, threads, dev, cus, stream);
+            return;
+        }
+    }
+    launch_fused_pack_as<E, R, PPT, BOUND, false>(a, grid, threads, dev, cus, stream);
 }
 
 template <class E, int R>

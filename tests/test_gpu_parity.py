@@ -215,11 +215,13 @@ def test_fused_widths(dtype, hidden):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [2048, 4096, 5120, 8192, 10240, 12288, 14336, 16384])
+@pytest.mark.parametrize("hidden", [2048, 3072, 4096, 5120, 7168, 8192, 10240, 12288, 14336, 16384])
 def test_fused_widths_at_the_layout_switch(dtype, hidden):
     """Up to one row per CU the register-row kernel takes its latency layout
     (up to 1024 lanes a row); with more rows, its throughput layout (up to 512
-    lanes, 1..8 packs per lane). The row count at the switch and one past it."""
+    lanes, 1..8 packs per lane; 128 lanes for rows of 384 and 640 packs). Rows
+    that fill every lane's slots take the pipelined full-row variant. The row
+    count at the switch and one past it."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for rows in (cus, cus + 1):
         note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
@@ -260,6 +262,24 @@ def test_fused_aliasing(dtype):
     torch.cuda.synchronize()
     assert_bitexact(host_bits(res), ref_inter, dtype, "intermediate in place of the residual")
     assert_output_close(host_bits(parts[1]), ref_out, dtype, "output in place of partial 1")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("hidden", [3072, 5120, 8192])
+def test_fused_aliasing_in_the_full_row_variant(dtype, hidden):
+    """More rows than CUs, rows that fill every slot (the full-row variant,
+    whose S stores come after all of a row's loads): intermediate ==
+    residual and output == a partial still give the oracle's results."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    w = inputs.random_fused(dtype, 8, cus + 3, hidden, 720)
+    ref_out, ref_inter = ref_fused(w)
+    parts = [dev(p, dtype) for p in w.partials]
+    res = dev(w.residual, dtype)
+    ar.ar_residual_rmsnorm(parts, dev(w.weight, dtype), w.eps, parts[5], res, bias=dev(w.bias, dtype),
+                           residual=res)
+    torch.cuda.synchronize()
+    assert_bitexact(host_bits(res), ref_inter, dtype, "intermediate in place of the residual")
+    assert_output_close(host_bits(parts[5]), ref_out, dtype, "output in place of partial 5")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
