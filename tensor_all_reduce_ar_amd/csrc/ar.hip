@@ -82,7 +82,7 @@ constexpr int kMaxPPT = 8;
 constexpr int kFusedMaxThreads = 1024;
 constexpr int kLatencyMaxPPT = 2;
 constexpr int kFullMaxPPT = 5;   // full-row variant: slots per lane, at most
-constexpr int kFullLanes = 128;  // full-row variant: workgroup size
+constexpr int kFullLanes = 128;  // full-row variant: workgroup size, at most
 constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
 constexpr int kElemThreads = 256;       // element-wise kernels
 constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
@@ -668,18 +668,25 @@ struct FusedGeometry {
 };
 
 // Throughput layout: 1 pack per lane up to 512 packs, 2 up to 1024, then
-// ceil(ppr / 256) up to kMaxPPT. Where that workgroup would hold 3, 5, 6 or 7
-// waves (so a CU's 4 SIMDs get unequal shares) and the row is 3 or 5 blocks of
-// 128 packs, it takes 128 lanes with 3 or 5 packs each instead: measured
-// 2-8 % faster on rows of 384 and 640 packs (for 16-bit types, hidden 3072
-// and 5120), where 7 blocks (896 packs) measured slower. Latency layout
-// (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024) packs per lane,
-// up to kLatencyMaxPPT.
+// ceil(ppr / 256) up to kMaxPPT. Three row widths would get workgroups of 5 or
+// 6 waves, which a CU's four SIMDs share unequally; they take 64 or 128 lanes
+// with 3 or 5 packs each instead (the pipelined full-row variant): rows of
+// 320, 384 and 640 packs (hidden 2560, 3072 and 5120 in 16-bit types) measured
+// 3-9 % faster so. Rows of 768 packs (6 waves of 2 packs) gained at most 2 %
+// and rows of 896 (7 waves) lost on 128 lanes, so they keep the default.
+// Latency layout (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024)
+// packs per lane, up to kLatencyMaxPPT.
 FusedGeometry fused_geometry(int ppr, bool few_rows)
 {
     int k, bound;
-    if (!few_rows && (ppr == 3 * kFullLanes || ppr == 5 * kFullLanes))
-        return FusedGeometry{ppr / kFullLanes, kFullLanes, 256};
+    if (!few_rows) {
+        switch (ppr) {
+        case 320: return FusedGeometry{5, 64, 256};
+        case 384: return FusedGeometry{3, 128, 256};
+        case 640: return FusedGeometry{5, 128, 256};
+        default: break;
+        }
+    }
     if (few_rows && ppr > 512 && ppr <= kLatencyMaxPPT * kFusedMaxThreads) {
         k = (ppr + kFusedMaxThreads - 1) / kFusedMaxThreads;
         bound = kFusedMaxThreads;
@@ -829,15 +836,15 @@ void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int de
 }
 
 // The pipelined full-row variant runs where it was measured faster: the
-// 128-lane layout (3 or 5 packs per lane, the rows of 384 and 640 packs), 2-9 %
-// over the plain slots. With one or two slots on 512 lanes (rows of 512 and
-// 1024 packs) it was as fast or up to 7 % slower: two slots' loads in flight
-// per lane cost more there than the overlap gains.
+// narrow layouts of 64 or 128 lanes with 3 or 5 packs per lane (rows of 320,
+// 384 and 640 packs). With one or two slots on 512 lanes (rows of 512 and 1024
+// packs) it was as fast or up to 7 % slower: two slots' loads in flight per
+// lane cost more there than the overlap gains.
 template <class E, int R, int PPT, int BOUND>
 void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
 {
     if constexpr (PPT >= 3 && PPT <= kFullMaxPPT) {
-        if (threads == kFullLanes && a.ppr == PPT * threads) {
+        if (threads <= kFullLanes && a.ppr == PPT * threads) {
             launch_fused_pack_as<E, R, PPT, BOUND, true>(a, grid, threads, dev, cus, stream);
             return;
         }

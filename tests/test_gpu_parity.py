@@ -215,13 +215,13 @@ def test_fused_widths(dtype, hidden):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [2048, 3072, 4096, 5120, 7168, 8192, 10240, 12288, 14336, 16384])
+@pytest.mark.parametrize("hidden", [2048, 2560, 3072, 4096, 5120, 6144, 7168, 8192, 10240, 12288, 14336, 16384])
 def test_fused_widths_at_the_layout_switch(dtype, hidden):
     """Up to one row per CU the register-row kernel takes its latency layout
     (up to 1024 lanes a row); with more rows, its throughput layout (up to 512
-    lanes, 1..8 packs per lane; 128 lanes for rows of 384 and 640 packs). Rows
-    that fill every lane's slots take the pipelined full-row variant. The row
-    count at the switch and one past it."""
+    lanes, 1..8 packs per lane; 64 or 128 lanes, pipelined full-row variant,
+    for rows of 320, 384 and 640 packs). The row count at the switch and one
+    past it."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for rows in (cus, cus + 1):
         note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
@@ -265,7 +265,7 @@ def test_fused_aliasing(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [3072, 5120, 8192])
+@pytest.mark.parametrize("hidden", [2560, 3072, 5120, 8192])
 def test_fused_aliasing_in_the_full_row_variant(dtype, hidden):
     """More rows than CUs, rows that fill every slot (the full-row variant,
     whose S stores come after all of a row's loads): intermediate ==
