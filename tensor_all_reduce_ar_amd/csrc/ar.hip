@@ -24,11 +24,14 @@
 //    v_cvt_pk_f16_f32); no multiply sits in the sum, so no contraction can
 //    change it, and fp32 denormals are kept (the kernels' default mode);
 //  * the fused op runs one workgroup per row with the row held in registers:
-//    S is stored as soon as it is formed, the sum of squares of the rounded S
-//    is reduced with cross-lane shuffles inside each 64-wide wave, then
-//    through LDS across waves with a single barrier, and the normed row is
-//    written from registers - each input is read once and each output written
-//    once.
+//    S is stored once it is formed, the sum of squares of the rounded S is
+//    reduced with cross-lane shuffles inside each 64-wide wave, then through
+//    LDS across waves with a single barrier, and the normed row is written
+//    from registers - each input is read once and each output written once;
+//  * the workgroup shape follows the row width: whole power-of-two numbers of
+//    waves per workgroup where the width allows (the four SIMDs of a CU get
+//    equal shares), more lanes per row when there are too few rows to fill
+//    the chip.
 // Shapes the vector path does not cover (pointers not 16-byte aligned, rows
 // whose byte size is not a multiple of 16, rows wider than the register
 // budget) run element-wise kernels with the same arithmetic.
@@ -74,7 +77,8 @@ constexpr int kSumThreads = AR_SUM_THREADS;
 // Register-row fused kernel, two layouts. Throughput layout (more rows than
 // CUs): a row of up to 1024 packs takes 1 or 2 packs per lane on up to 512
 // lanes; wider rows (up to 2048 packs) take 3..8 packs per lane on up to 256
-// lanes, which keeps every variant within the VGPR budget of its launch bound.
+// lanes, which keeps every variant within the VGPR budget of its launch bound;
+// rows of 320, 384 and 640 packs take 64 or 128 lanes (see fused_geometry).
 // Latency layout (no more rows than CUs, rows of 513..2048 packs): up to 1024
 // lanes, so each lane's packs - and so the memory round trips of a row - are
 // halved when the chip is not full anyway.
