@@ -844,16 +844,22 @@ void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int de
 // 384 and 640 packs). With one or two slots on 512 lanes (rows of 512 and 1024
 // packs) it was as fast or up to 7 % slower: two slots' loads in flight per
 // lane cost more there than the overlap gains.
+// Returns false, launching nothing, if the shape does not fit the instance: a
+// workgroup larger than the launch bound would index `part` past its end and
+// exceed the registers the kernel was compiled for, and lanes must cover the row.
 template <class E, int R, int PPT, int BOUND>
-void launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
+bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
 {
+    if (threads < kWave || threads > BOUND || threads % kWave != 0 || PPT * threads < a.ppr)
+        return false;
     if constexpr (PPT >= 3 && PPT <= kFullMaxPPT) {
         if (threads <= kFullLanes && a.ppr == PPT * threads) {
             launch_fused_pack_as<E, R, PPT, BOUND, true>(a, grid, threads, dev, cus, stream);
-            return;
+            return true;
         }
     }
     launch_fused_pack_as<E, R, PPT, BOUND, false>(a, grid, threads, dev, cus, stream);
+    return true;
 }
 
 template <class E, int R>
@@ -890,25 +896,28 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
             fprintf(stderr, "[ar] fused pack R=%d rows=%zu H=%d ppr=%d ppt=%d block=%d bound=%d grid=%u\n", R,
                     a.rows, a.hidden, a.ppr, g.ppt, g.threads, g.bound, grid);
         const int t = g.threads;
+        bool ok = false;
         if (g.bound == kFusedMaxThreads) {
             switch (g.ppt) {
-            case 1: launch_fused_pack<E, R, 1, kFusedMaxThreads>(a, grid, t, dev, cus, stream); break;
-            case 2: launch_fused_pack<E, R, 2, kFusedMaxThreads>(a, grid, t, dev, cus, stream); break;
-            default: return AR_ERR_SHAPE;  // unreachable: the latency layout yields 1..kLatencyMaxPPT
+            case 1: ok = launch_fused_pack<E, R, 1, kFusedMaxThreads>(a, grid, t, dev, cus, stream); break;
+            case 2: ok = launch_fused_pack<E, R, 2, kFusedMaxThreads>(a, grid, t, dev, cus, stream); break;
+            default: break;
             }
         } else {
             switch (g.ppt) {
-            case 1: launch_fused_pack<E, R, 1, 512>(a, grid, t, dev, cus, stream); break;
-            case 2: launch_fused_pack<E, R, 2, 512>(a, grid, t, dev, cus, stream); break;
-            case 3: launch_fused_pack<E, R, 3, 256>(a, grid, t, dev, cus, stream); break;
-            case 4: launch_fused_pack<E, R, 4, 256>(a, grid, t, dev, cus, stream); break;
-            case 5: launch_fused_pack<E, R, 5, 256>(a, grid, t, dev, cus, stream); break;
-            case 6: launch_fused_pack<E, R, 6, 256>(a, grid, t, dev, cus, stream); break;
-            case 7: launch_fused_pack<E, R, 7, 256>(a, grid, t, dev, cus, stream); break;
-            case 8: launch_fused_pack<E, R, 8, 256>(a, grid, t, dev, cus, stream); break;
-            default: return AR_ERR_SHAPE;  // unreachable: fused_geometry yields 0..kMaxPPT
+            case 1: ok = launch_fused_pack<E, R, 1, 512>(a, grid, t, dev, cus, stream); break;
+            case 2: ok = launch_fused_pack<E, R, 2, 512>(a, grid, t, dev, cus, stream); break;
+            case 3: ok = launch_fused_pack<E, R, 3, 256>(a, grid, t, dev, cus, stream); break;
+            case 4: ok = launch_fused_pack<E, R, 4, 256>(a, grid, t, dev, cus, stream); break;
+            case 5: ok = launch_fused_pack<E, R, 5, 256>(a, grid, t, dev, cus, stream); break;
+            case 6: ok = launch_fused_pack<E, R, 6, 256>(a, grid, t, dev, cus, stream); break;
+            case 7: ok = launch_fused_pack<E, R, 7, 256>(a, grid, t, dev, cus, stream); break;
+            case 8: ok = launch_fused_pack<E, R, 8, 256>(a, grid, t, dev, cus, stream); break;
+            default: break;
             }
         }
+        if (!ok)
+            return AR_ERR_SHAPE;  // unreachable: fused_geometry only yields shapes the instances take
     } else {
         if (log_enabled())
             fprintf(stderr, "[ar] fused elem R=%d rows=%zu H=%d grid=%u\n", R, a.rows, a.hidden, grid);
