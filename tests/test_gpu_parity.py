@@ -370,3 +370,52 @@ def test_concurrent_streams_do_not_interfere():
         assert np.array_equal(host_bits(o), want[0])
         assert np.array_equal(host_bits(i), want[1])
         assert np.array_equal(host_bits(s), want[2])
+
+
+def test_calls_from_several_host_threads():
+    """The entry points are re-entrant: host threads, each with its own stream
+    and its own shapes (different kernel instances, so first calls fill the
+    per-device caches at the same time), all match the oracle."""
+    import threading
+    cases = [inputs.random_fused("bf16", 8, 300, 5120, 1700), inputs.random_fused("fp16", 3, 270, 3072, 1701),
+             inputs.random_fused("fp32", 6, 300, 2560, 1702), inputs.random_fused("bf16", 5, 260, 12288, 1703)]
+    sums = [inputs.random_sum("fp16", 7, 300007, 1704), inputs.random_sum("fp32", 5, 200003, 1705)]
+    jobs = []
+    for w in cases:
+        parts = [dev(p, w.dtype) for p in w.partials]
+        bufs = (torch.empty_like(parts[0]), torch.empty_like(parts[0]))
+        jobs.append(("fused", w, parts, bufs, (dev(w.weight, w.dtype), dev(w.bias, w.dtype), dev(w.residual, w.dtype))))
+    for w in sums:
+        parts = [dev(p, w.dtype) for p in w.partials]
+        jobs.append(("sum", w, parts, (torch.empty_like(parts[0]),), None))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(job):
+        try:
+            kind, w, parts, bufs, extra = job
+            stream = torch.cuda.Stream()
+            for _ in range(5):
+                if kind == "fused":
+                    weight, bias, res = extra
+                    ar.ar_residual_rmsnorm(parts, weight, w.eps, bufs[0], bufs[1], bias=bias, residual=res,
+                                           stream=stream)
+                else:
+                    ar.ar_sum(parts, bufs[0], stream=stream)
+            stream.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for kind, w, parts, bufs, extra in jobs:
+        note(f"[parity] threads {kind} {w.name}")
+        if kind == "fused":
+            check_fused(w, host_bits(bufs[0]), host_bits(bufs[1]))
+        else:
+            assert_bitexact(host_bits(bufs[0]), ref_sum(w), w.dtype, f"threaded {w.name}")
