@@ -87,6 +87,7 @@ constexpr int kFusedMaxThreads = 1024;
 constexpr int kLatencyMaxPPT = 2;
 constexpr int kFullMaxPPT = 5;   // full-row variant: slots per lane, at most
 constexpr int kFullLanes = 128;  // full-row variant: workgroup size, at most
+constexpr int kRowsMaxPacks = 512;  // multi-row kernel: widest row, and workgroup size bound
 constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
 constexpr int kElemThreads = 256;       // element-wise kernels
 constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
@@ -481,6 +482,72 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
     }
 }
 
+// Fused op for narrow rows (up to kRowsMaxPacks packs) when they outnumber
+// the CUs: a workgroup takes NR adjacent rows per iteration, one pack per lane
+// of each, so an iteration moves NR rows of every buffer together and the NR
+// row sums share one barrier. Lane j holds column pack j of every row (weight
+// and bias packs are loaded once); lanes past the row and rows past the end
+// take no part. Same arithmetic as the other fused kernels.
+template <class E, int R, int NR>
+__global__ __launch_bounds__(kRowsMaxPacks) void ar_rmsnorm_rows_kernel(FusedArgs a)
+{
+    __shared__ float part[NR][kRowsMaxPacks / kWave];
+    const u32x4 *bias = static_cast<const u32x4 *>(a.bias);
+    const int j = threadIdx.x;
+    const bool active = j < a.ppr;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    const size_t groups = (a.rows + NR - 1) / NR;
+    u32x4 w = {0, 0, 0, 0}, bq = {0, 0, 0, 0};
+    if (active) {
+        w = static_cast<const u32x4 *>(a.weight)[j];
+        if (bias)
+            bq = bias[j];
+    }
+    for (size_t g = blockIdx.x; g < groups; g += gridDim.x) {
+        u32x4 sp[NR];
+        float ss[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            ss[k] = 0.0f;
+            const size_t row = g * NR + k;
+            if (active && row < a.rows) {
+                const size_t off = row * static_cast<size_t>(a.ppr) + j;
+                u32x4 v[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    v[r] = ld16(static_cast<const u32x4 *>(a.in[r]) + off);
+                u32x4 rq = {0, 0, 0, 0};
+                if (a.residual)
+                    rq = ld16(static_cast<const u32x4 *>(a.residual) + off);
+                sp[k] = fused_pre_norm<E, R>(v, bias != nullptr, bq, a.residual != nullptr, rq);
+                st16(static_cast<u32x4 *>(a.inter) + off, sp[k]);
+                ss[k] = sum_squares<E>(sp[k]);
+            }
+        }
+        // one barrier for the NR sums; every lane adds the wave partials in
+        // the same order
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const float x = wave_sum(ss[k]);
+            if (lane == 0)
+                part[k][wave] = x;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            float t = part[k][0];
+            for (int q = 1; q < nw; ++q)
+                t = t + part[k][q];
+            const float rstd = rms_scale(t, a.hidden, a.eps);
+            const size_t row = g * NR + k;
+            if (active && row < a.rows)
+                st16(static_cast<u32x4 *>(a.out) + row * static_cast<size_t>(a.ppr) + j,
+                     normed_pack<E>(sp[k], rstd, w));
+        }
+        __syncthreads();  // `part` is rewritten by the next group
+    }
+}
+
 // Fused op for rows wider than the register path, still 16-byte packs: pass
 // 1 forms, stores and squares S; pass 2 re-reads the S packs this lane stored
 // (normal stores, so they are likely still in L2) and writes the norm.
@@ -669,15 +736,21 @@ struct FusedGeometry {
     int ppt;      // packs per lane; 0 = the row is too wide, the wide kernel takes it
     int threads;  // workgroup size: the fewest whole waves that cover the row
     int bound;    // launch bound of the kernel instance (512, 256 or 1024)
+    int rows = 1; // rows per workgroup iteration: > 1 selects the multi-row kernel
 };
 
-// Throughput layout: 1 pack per lane up to 512 packs, 2 up to 1024, then
-// ceil(ppr / 256) up to kMaxPPT. Three row widths would get workgroups of 5 or
-// 6 waves, which a CU's four SIMDs share unequally; they take 64 or 128 lanes
-// with 3 or 5 packs each instead (the pipelined full-row variant): rows of
-// 320, 384 and 640 packs (hidden 2560, 3072 and 5120 in 16-bit types) measured
-// 3-9 % faster so. Rows of 768 packs (6 waves of 2 packs) gained at most 2 %
-// and rows of 896 (7 waves) lost on 128 lanes, so they keep the default.
+// Throughput layout: rows of 256 and 512 packs take the multi-row kernel (one
+// pack per lane, 4 or 2 adjacent rows per iteration): measured 2-7 % faster
+// than one row per iteration on hidden 2048 and 4096 in 16-bit types (as fast
+// on 2048 in fp32). Rows of 128 and 448 packs measured 3-5 % slower so; other
+// rows up to 512 packs keep one row per iteration, 1 pack per lane. Wider
+// rows: 2 packs per lane up to 1024, then ceil(ppr / 256) up to kMaxPPT. Three row
+// widths would get workgroups of 5 or 6 waves, which a CU's four SIMDs share
+// unequally; they take 64 or 128 lanes with 3 or 5 packs each instead (the
+// pipelined full-row variant): rows of 320, 384 and 640 packs (hidden 2560,
+// 3072 and 5120 in 16-bit types) measured 3-9 % faster so. Rows of 768 packs
+// (6 waves of 2 packs) gained at most 2 % and rows of 896 (7 waves) lost on
+// 128 lanes, so they keep the default.
 // Latency layout (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024)
 // packs per lane, up to kLatencyMaxPPT.
 FusedGeometry fused_geometry(int ppr, bool few_rows)
@@ -690,6 +763,8 @@ FusedGeometry fused_geometry(int ppr, bool few_rows)
         case 640: return FusedGeometry{5, 128, 256};
         default: break;
         }
+        if (ppr == 256 || ppr == kRowsMaxPacks)
+            return FusedGeometry{1, ppr, kRowsMaxPacks, ppr == 256 ? 4 : 2};
     }
     if (few_rows && ppr > 512 && ppr <= kLatencyMaxPPT * kFusedMaxThreads) {
         k = (ppr + kFusedMaxThreads - 1) / kFusedMaxThreads;
@@ -862,6 +937,22 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
     return true;
 }
 
+// Multi-row kernel on a resident grid (no more workgroups than row groups).
+// Returns false, launching nothing, if the workgroup does not fit the kernel.
+template <class E, int R, int NR>
+bool launch_fused_rows(const FusedArgs &a, int threads, int dev, int cus, hipStream_t stream)
+{
+    if (threads < kWave || threads > kRowsMaxPacks || threads % kWave != 0 || threads < a.ppr)
+        return false;
+    static OccCache occ;
+    const size_t resident =
+        static_cast<size_t>(cus) * resident_per_cu(ar_rmsnorm_rows_kernel<E, R, NR>, threads, dev, occ);
+    const size_t groups = (a.rows + NR - 1) / NR;
+    const unsigned grid = clamp_grid(groups < resident ? groups : resident);
+    hipLaunchKernelGGL((ar_rmsnorm_rows_kernel<E, R, NR>), dim3(grid), dim3(threads), 0, stream, a);
+    return true;
+}
+
 template <class E, int R>
 int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
 {
@@ -886,7 +977,19 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
         cus = device_cus(dev);
         g = fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus));
     }
-    if (vec && g.ppt == 0) {
+    if (vec && g.rows > 1) {
+        if (log_enabled())
+            fprintf(stderr, "[ar] fused rows R=%d rows=%zu H=%d ppr=%d rows/iter=%d block=%d\n", R, a.rows, a.hidden,
+                    a.ppr, g.rows, g.threads);
+        bool ok = false;
+        switch (g.rows) {
+        case 2: ok = launch_fused_rows<E, R, 2>(a, g.threads, dev, cus, stream); break;
+        case 4: ok = launch_fused_rows<E, R, 4>(a, g.threads, dev, cus, stream); break;
+        default: break;
+        }
+        if (!ok)
+            return AR_ERR_SHAPE;  // unreachable: fused_geometry only yields shapes the kernel takes
+    } else if (vec && g.ppt == 0) {
         if (log_enabled())
             fprintf(stderr, "[ar] fused wide R=%d rows=%zu H=%d ppr=%d block=%d grid=%u\n", R, a.rows, a.hidden,
                     a.ppr, kWideThreads, grid);
