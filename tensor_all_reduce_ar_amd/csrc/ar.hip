@@ -482,6 +482,48 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
     }
 }
 
+// Fused op for narrow rows of exactly 64 * SL packs when they outnumber the
+// CUs: one wave per row and no barrier at all. The row's sum of squares is
+// reduced inside the wave (xor butterfly), so waves never wait for each other;
+// a workgroup's W waves take W adjacent rows. Lane l holds packs l + 64 p; the
+// slots are software-pipelined two deep like the full-row variant (next
+// slot's loads before this slot's sums, a compiler fence per slot, S stored
+// after the row's last load).
+template <class E, int R, int SL, int W>
+__global__ __launch_bounds__(W * kWave) void ar_rmsnorm_wave_kernel(FusedArgs a)
+{
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const u32x4 *bias = static_cast<const u32x4 *>(a.bias);
+    const u32x4 *weight = static_cast<const u32x4 *>(a.weight);
+    const size_t stride = static_cast<size_t>(gridDim.x) * W;
+    for (size_t row = static_cast<size_t>(blockIdx.x) * W + wave; row < a.rows; row += stride) {
+        const size_t row0 = row * static_cast<size_t>(a.ppr);
+        u32x4 sp[SL], v[2][R], rq[2];
+        float ss = 0.0f;
+        load_slot<R>(a, row0 + lane, v[0], rq[0]);
+#pragma unroll
+        for (int p = 0; p < SL; ++p) {
+            const int j = lane + p * kWave;
+            if (p + 1 < SL)
+                load_slot<R>(a, row0 + j + kWave, v[(p + 1) & 1], rq[(p + 1) & 1]);
+            const u32x4 bq = bias ? bias[j] : u32x4{0, 0, 0, 0};
+            sp[p] = fused_pre_norm<E, R>(v[p & 1], bias != nullptr, bq, a.residual != nullptr, rq[p & 1]);
+            ss += sum_squares<E>(sp[p]);
+            asm volatile("" ::: "memory");
+        }
+#pragma unroll
+        for (int p = 0; p < SL; ++p)
+            st16(static_cast<u32x4 *>(a.inter) + row0 + lane + p * kWave, sp[p]);
+        const float rstd = rms_scale(wave_sum(ss), a.hidden, a.eps);
+#pragma unroll
+        for (int p = 0; p < SL; ++p) {
+            const int j = lane + p * kWave;
+            st16(static_cast<u32x4 *>(a.out) + row0 + j, normed_pack<E>(sp[p], rstd, weight[j]));
+        }
+    }
+}
+
 // Fused op for narrow rows (up to kRowsMaxPacks packs) when they outnumber
 // the CUs: a workgroup takes NR adjacent rows per iteration, one pack per lane
 // of each, so an iteration moves NR rows of every buffer together and the NR
@@ -737,13 +779,17 @@ struct FusedGeometry {
     int threads;  // workgroup size: the fewest whole waves that cover the row
     int bound;    // launch bound of the kernel instance (512, 256 or 1024)
     int rows = 1; // rows per workgroup iteration: > 1 selects the multi-row kernel
+    int waves = 0; // > 0 selects the wave-per-row kernel, with this many waves (rows) per workgroup
 };
 
-// Throughput layout: rows of 256 and 512 packs take the multi-row kernel (one
-// pack per lane, 4 or 2 adjacent rows per iteration): measured 2-7 % faster
-// than one row per iteration on hidden 2048 and 4096 in 16-bit types (as fast
-// on 2048 in fp32). Rows of 128 and 448 packs measured 3-5 % slower so; other
-// rows up to 512 packs keep one row per iteration, 1 pack per lane. Wider
+// Throughput layout: rows of 128 and 256 packs take the wave-per-row kernel
+// (2 or 4 packs per lane, 8 or 4 rows per workgroup, no barrier): measured
+// 5-7 % faster than one workgroup per row on hidden 1024 and 2048 in 16-bit
+// types. Rows of 512 packs take the multi-row kernel (one pack per lane, 2
+// adjacent rows per iteration, one barrier): 1.5-4 % faster on hidden 4096
+// in 16-bit types, where the wave-per-row kernel (8 packs per lane) was
+// slower. Other rows up to 512 packs keep one row per workgroup, 1 pack per
+// lane (4 rows per iteration measured 3-5 % slower at 448 packs). Wider
 // rows: 2 packs per lane up to 1024, then ceil(ppr / 256) up to kMaxPPT. Three row
 // widths would get workgroups of 5 or 6 waves, which a CU's four SIMDs share
 // unequally; they take 64 or 128 lanes with 3 or 5 packs each instead (the
@@ -763,8 +809,13 @@ FusedGeometry fused_geometry(int ppr, bool few_rows)
         case 640: return FusedGeometry{5, 128, 256};
         default: break;
         }
-        if (ppr == 256 || ppr == kRowsMaxPacks)
-            return FusedGeometry{1, ppr, kRowsMaxPacks, ppr == 256 ? 4 : 2};
+        if (ppr == 128 || ppr == 256) {
+            FusedGeometry g{ppr / kWave, ppr == 128 ? 8 * kWave : 4 * kWave, 512};
+            g.waves = g.threads / kWave;
+            return g;
+        }
+        if (ppr == kRowsMaxPacks)
+            return FusedGeometry{1, ppr, kRowsMaxPacks, 2};
     }
     if (few_rows && ppr > 512 && ppr <= kLatencyMaxPPT * kFusedMaxThreads) {
         k = (ppr + kFusedMaxThreads - 1) / kFusedMaxThreads;
@@ -937,6 +988,22 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
     return true;
 }
 
+// Wave-per-row kernel on a resident grid (no more workgroups than row groups).
+// Returns false, launching nothing, unless the row is exactly SL packs per lane.
+template <class E, int R, int SL, int W>
+bool launch_fused_waves(const FusedArgs &a, int dev, int cus, hipStream_t stream)
+{
+    if (a.ppr != SL * kWave)
+        return false;
+    static OccCache occ;
+    const size_t resident =
+        static_cast<size_t>(cus) * resident_per_cu(ar_rmsnorm_wave_kernel<E, R, SL, W>, W * kWave, dev, occ);
+    const size_t groups = (a.rows + W - 1) / W;
+    const unsigned grid = clamp_grid(groups < resident ? groups : resident);
+    hipLaunchKernelGGL((ar_rmsnorm_wave_kernel<E, R, SL, W>), dim3(grid), dim3(W * kWave), 0, stream, a);
+    return true;
+}
+
 // Multi-row kernel on a resident grid (no more workgroups than row groups).
 // Returns false, launching nothing, if the workgroup does not fit the kernel.
 template <class E, int R, int NR>
@@ -977,7 +1044,18 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
         cus = device_cus(dev);
         g = fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus));
     }
-    if (vec && g.rows > 1) {
+    if (vec && g.waves > 0) {
+        if (log_enabled())
+            fprintf(stderr, "[ar] fused wave-per-row R=%d rows=%zu H=%d ppr=%d waves/block=%d\n", R, a.rows,
+                    a.hidden, a.ppr, g.waves);
+        bool ok = false;
+        if (g.ppt == 2 && g.waves == 8)
+            ok = launch_fused_waves<E, R, 2, 8>(a, dev, cus, stream);
+        else if (g.ppt == 4 && g.waves == 4)
+            ok = launch_fused_waves<E, R, 4, 4>(a, dev, cus, stream);
+        if (!ok)
+            return AR_ERR_SHAPE;  // unreachable: fused_geometry only yields shapes the kernel takes
+    } else if (vec && g.rows > 1) {
         if (log_enabled())
             fprintf(stderr, "[ar] fused rows R=%d rows=%zu H=%d ppr=%d rows/iter=%d block=%d\n", R, a.rows, a.hidden,
                     a.ppr, g.rows, g.threads);

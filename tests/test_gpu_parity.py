@@ -215,12 +215,13 @@ def test_fused_widths(dtype, hidden):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [8, 64, 1000, 1024, 2000, 2048, 2560, 3072, 3584, 4096, 5120, 6144, 7168, 8192,
-                                    10240, 12288, 14336, 16384])
+@pytest.mark.parametrize("hidden", [8, 64, 512, 1000, 1024, 2000, 2048, 2560, 3072, 3584, 4096, 5120, 6144, 7168,
+                                    8192, 10240, 12288, 14336, 16384])
 def test_fused_widths_at_the_layout_switch(dtype, hidden):
     """Up to one row per CU the register-row kernel takes its latency layout
-    (up to 1024 lanes a row). With more rows: the multi-row kernel for rows of
-    256..512 packs (2 or 4 rows per iteration; the last group may be short),
+    (up to 1024 lanes a row). With more rows: one wave per row for rows of 128
+    and 256 packs (8 or 4 rows per workgroup; the last group may be short),
+    the multi-row kernel for rows of 512 packs (2 rows per iteration),
     64 or 128 lanes in the pipelined full-row variant for rows of 320, 384 and
     640 packs, and up to 512 lanes with 1..8 packs per lane for the rest. The
     row count at the switch and one past it."""
@@ -267,11 +268,12 @@ def test_fused_aliasing(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [1024, 2048, 2560, 3072, 4096, 5120, 8192])
+@pytest.mark.parametrize("hidden", [512, 1024, 2048, 2560, 3072, 4096, 5120, 8192])
 def test_fused_aliasing_in_the_throughput_layouts(dtype, hidden):
-    """More rows than CUs (the multi-row kernel, the full-row variant whose S
-    stores come after all of a row's loads, the plain slots): intermediate ==
-    residual and output == a partial still give the oracle's results."""
+    """More rows than CUs (the wave-per-row and multi-row kernels, the full-row
+    variant whose S stores come after all of a row's loads, the plain slots):
+    intermediate == residual and output == a partial still give the oracle's
+    results."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     w = inputs.random_fused(dtype, 8, cus + 3, hidden, 720)
     ref_out, ref_inter = ref_fused(w)
