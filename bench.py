@@ -333,7 +333,10 @@ def stream_ceilings(torch, stream):
     copy. GB/s of bytes moved."""
     from tensor_all_reduce_ar_amd import stream_ceiling as sc
     n = 1 << 28  # fp32 elements, 1 GiB
-    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    # random contents: constant data streams measurably faster than real data
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    src = torch.randn(n, dtype=torch.float32, device="cuda", generator=gen)
     dst = torch.empty_like(src)
 
     def rate(fn, nbytes, reps=10):

@@ -1,8 +1,11 @@
 // stream_ceiling.hip - streaming-ceiling kernels for gfx950 (measurement only;
 // C ABI in stream_ceiling.h). Each call reads NI buffers and writes NO buffers
-// of the same size once, 16-byte non-temporal loads and stores, in one of a
-// few workgroup shapes (lanes x packs per lane per step), with no other work.
-// No single shape is fastest for every mix of streams, so a caller times each.
+// of the same size once, 16-byte non-temporal loads, in one of a few
+// workgroup shapes (lanes x packs per lane per step) and one of two store
+// forms, with no other work: non-temporal global stores, or buffer stores at
+// device scope (cache-policy field sc1) from the step's start address. No
+// single shape or store form is fastest for every mix of streams, so a caller
+// times each.
 
 #include <hip/hip_runtime.h>
 
@@ -36,10 +39,21 @@ __device__ __forceinline__ void one_pack(const StreamArgs &a, size_t j)
         asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
 }
 
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) 32-bit data format
+constexpr int kPolicySc1 = 16;            // cache-policy field: sc1 (device scope), temporal
+
+// Pack at byte offset `off` of the `extent` bytes from `base`; `base` is the
+// same in every lane of the wave.
+__device__ __forceinline__ void store_sc1(u32x4 *base, uint32_t off, uint32_t extent, u32x4 v)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(extent), kBufferWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kPolicySc1);
+}
+
 // kThreads lanes x kUnroll packs per step; consecutive steps go to
 // consecutive workgroups; the packs after the last full step are done by the
-// last workgroup.
-template <int NI, int NO, int kThreads, int kUnroll>
+// last workgroup. SC1: the full steps' stores are device-scope buffer stores.
+template <int NI, int NO, int kThreads, int kUnroll, bool SC1>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a)
 {
     const size_t step = static_cast<size_t>(kThreads) * kUnroll;
@@ -58,8 +72,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a)
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
-            for (int k = 0; k < NO; ++k)
-                __builtin_nontemporal_store(x[u], a.out[k] + base + u * kThreads);
+            for (int k = 0; k < NO; ++k) {
+                if (SC1)
+                    store_sc1(a.out[k] + c * step, (threadIdx.x + u * kThreads) * 16u, step * 16u, x[u]);
+                else
+                    __builtin_nontemporal_store(x[u], a.out[k] + base + u * kThreads);
+            }
             if (NO == 0)
                 asm volatile("" ::"v"(x[u].x), "v"(x[u].y), "v"(x[u].z), "v"(x[u].w));
         }
@@ -69,12 +87,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a)
             one_pack<NI, NO>(a, j);
 }
 
-template <int NI, int NO, int T, int U>
+template <int NI, int NO, int T, int U, bool SC1>
 int32_t launch(const StreamArgs &a, hipStream_t stream)
 {
     size_t blocks = a.npacks / (static_cast<size_t>(T) * U);
     const unsigned grid = blocks < 1 ? 1u : blocks > kMaxGrid ? kMaxGrid : static_cast<unsigned>(blocks);
-    hipLaunchKernelGGL((stream_kernel<NI, NO, T, U>), dim3(grid), dim3(T), 0, stream, a);
+    hipLaunchKernelGGL((stream_kernel<NI, NO, T, U, SC1>), dim3(grid), dim3(T), 0, stream, a);
     return hipGetLastError() == hipSuccess ? SC_OK : SC_ERR_HIP;
 }
 
@@ -82,10 +100,14 @@ template <int NI, int NO>
 int32_t by_shape(int shape, const StreamArgs &a, hipStream_t s)
 {
     switch (shape) {
-    case SC_SHAPE_512x2: return launch<NI, NO, 512, 2>(a, s);
-    case SC_SHAPE_256x4: return launch<NI, NO, 256, 4>(a, s);
-    case SC_SHAPE_256x8: return launch<NI, NO, 256, 8>(a, s);
-    default: return launch<NI, NO, 128, 8>(a, s);
+    case SC_SHAPE_512x2: return launch<NI, NO, 512, 2, false>(a, s);
+    case SC_SHAPE_256x4: return launch<NI, NO, 256, 4, false>(a, s);
+    case SC_SHAPE_256x8: return launch<NI, NO, 256, 8, false>(a, s);
+    case SC_SHAPE_128x8: return launch<NI, NO, 128, 8, false>(a, s);
+    case SC_SHAPE_512x2_SC1: return launch<NI, NO, 512, 2, true>(a, s);
+    case SC_SHAPE_256x4_SC1: return launch<NI, NO, 256, 4, true>(a, s);
+    case SC_SHAPE_256x8_SC1: return launch<NI, NO, 256, 8, true>(a, s);
+    default: return launch<NI, NO, 128, 8, true>(a, s);
     }
 }
 

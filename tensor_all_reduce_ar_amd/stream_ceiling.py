@@ -2,9 +2,9 @@
 
 Measurement only: ``sc_stream(inputs, outputs, shape)`` reads every input
 tensor and writes every output tensor once (outputs = bitwise XOR of the
-inputs) with plain streaming code in one of SHAPES, so that timing it on an
-all-reduce call's own buffers, in every shape, gives that call's practical HBM
-ceiling.
+inputs) with plain streaming code in one of SHAPES (a workgroup shape and a
+store form), so that timing it on an all-reduce call's own buffers, in every
+shape, gives that call's practical HBM ceiling.
 """
 from __future__ import annotations
 
@@ -15,8 +15,10 @@ from typing import Optional, Sequence
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstream_ceiling.so")
 SC_MAX_IN, SC_MAX_OUT = 12, 2
 SC_OK = 0
-# SC_SHAPE_* of include/stream_ceiling.h: lanes x packs per lane per step
-SHAPES = {0: "512x2", 1: "256x4", 2: "256x8", 3: "128x8"}
+# SC_SHAPE_* of include/stream_ceiling.h: lanes x packs per lane per step;
+# "/sc1": device-scope buffer stores instead of non-temporal global stores
+SHAPES = {0: "512x2", 1: "256x4", 2: "256x8", 3: "128x8",
+          4: "512x2/sc1", 5: "256x4/sc1", 6: "256x8/sc1", 7: "128x8/sc1"}
 
 _lib: Optional[ctypes.CDLL] = None
 

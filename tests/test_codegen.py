@@ -9,7 +9,8 @@ disassembled with the ROCm LLVM tools, then checked for:
   * no register spills and no scratch (private segment) in any kernel;
   * the instructions the design relies on: 16-byte non-temporal vector loads
     and stores, and the packed round-to-nearest-even conversions to bf16 and
-    fp16.
+    fp16; in the streaming-ceiling library, both of its store forms
+    (non-temporal global stores and device-scope buffer stores).
 """
 import os
 import re
@@ -88,3 +89,12 @@ def test_vector_path_instructions(libar):
     ops = _mnemonics(asm)
     assert "v_cvt_pk_bf16_f32" in ops, "packed RNE conversion to bf16"
     assert "v_cvt_pk_f16_f32" in ops, "packed RNE conversion to fp16"
+
+
+def test_ceiling_store_forms(libceiling):
+    asm, _ = libceiling
+    assert re.search(r"global_load_dwordx4 .* nt", asm), "16-byte non-temporal loads"
+    assert re.search(r"global_store_dwordx4 .* nt", asm), "16-byte non-temporal global stores"
+    sc1 = re.findall(r"buffer_store_dwordx4 .*", asm)
+    assert sc1, "16-byte buffer stores"
+    assert all(re.search(r"\bsc1\b", x) and not re.search(r"\b(nt|sc0)\b", x) for x in sc1), sc1[:3]
