@@ -77,7 +77,8 @@ constexpr int kSumThreads = AR_SUM_THREADS;
 // Register-row fused kernel, two layouts. Throughput layout (more rows than
 // CUs): a row of up to 1024 packs takes 1 or 2 packs per lane on up to 512
 // lanes; wider rows (up to 2048 packs) take 3..8 packs per lane on up to 256
-// lanes, which keeps every variant within the VGPR budget of its launch bound;
+// lanes, which keeps every variant within the VGPR budget of its launch bound
+// (those that fill every slot of every lane - 5..8 x 256 - run pipelined);
 // rows of 320, 384 and 640 packs take 64 or 128 lanes (see fused_geometry).
 // Latency layout (no more rows than CUs, rows of 513..2048 packs): up to 1024
 // lanes, so each lane's packs - and so the memory round trips of a row - are
@@ -85,8 +86,8 @@ constexpr int kSumThreads = AR_SUM_THREADS;
 constexpr int kMaxPPT = 8;
 constexpr int kFusedMaxThreads = 1024;
 constexpr int kLatencyMaxPPT = 2;
-constexpr int kFullMaxPPT = 5;   // full-row variant: slots per lane, at most
-constexpr int kFullLanes = 128;  // full-row variant: workgroup size, at most
+constexpr int kFullMaxPPT = 8;   // full-row variant: slots per lane, at most
+constexpr int kFullLanes = 256;  // full-row variant: workgroup size, at most
 constexpr int kRowsMaxPacks = 512;  // multi-row kernel: widest row, and workgroup size bound
 constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
 constexpr int kElemThreads = 256;       // element-wise kernels
@@ -796,7 +797,8 @@ struct FusedGeometry {
 // pipelined full-row variant): rows of 320, 384 and 640 packs (hidden 2560,
 // 3072 and 5120 in 16-bit types) measured 3-9 % faster so. Rows of 768 packs
 // (6 waves of 2 packs) gained at most 2 % and rows of 896 (7 waves) lost on
-// 128 lanes, so they keep the default.
+// 128 lanes, so they keep the default. Rows of 1280, 1536, 1792 and 2048
+// packs fill 5..8 packs on 256 lanes exactly and so run pipelined too.
 // Latency layout (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024)
 // packs per lane, up to kLatencyMaxPPT.
 FusedGeometry fused_geometry(int ppr, bool few_rows)
@@ -967,9 +969,12 @@ void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int de
 
 // The pipelined full-row variant runs where it was measured faster: the
 // narrow layouts of 64 or 128 lanes with 3 or 5 packs per lane (rows of 320,
-// 384 and 640 packs). With one or two slots on 512 lanes (rows of 512 and 1024
-// packs) it was as fast or up to 7 % slower: two slots' loads in flight per
-// lane cost more there than the overlap gains.
+// 384 and 640 packs, 3-9 % faster), and 256 lanes with 5..8 packs per lane
+// (rows of 1280, 1536, 1792 and 2048 packs: hidden 10240..16384 in 16-bit
+// types, 4-13 % faster than one round trip per slot). With one or two slots
+// on 512 lanes (rows of 512 and 1024 packs) it was as fast or up to 7 %
+// slower: two slots' loads in flight per lane cost more there than the
+// overlap gains.
 // Returns false, launching nothing, if the shape does not fit the instance: a
 // workgroup larger than the launch bound would index `part` past its end and
 // exceed the registers the kernel was compiled for, and lanes must cover the row.
