@@ -78,7 +78,8 @@ constexpr int kSumThreads = AR_SUM_THREADS;
 // CUs): a row of up to 1024 packs takes 1 or 2 packs per lane on up to 512
 // lanes; wider rows (up to 2048 packs) take 3..8 packs per lane on up to 256
 // lanes, which keeps every variant within the VGPR budget of its launch bound
-// (those that fill every slot of every lane - 5..8 x 256 - run pipelined);
+// (those that fill every slot of every lane - 5..8 x 256 - run pipelined, and
+// so do rows of exactly 1024 packs, as 4 x 256);
 // rows of 320, 384 and 640 packs take 64 or 128 lanes (see fused_geometry).
 // Latency layout (no more rows than CUs, rows of 513..2048 packs): up to 1024
 // lanes, so each lane's packs - and so the memory round trips of a row - are
@@ -791,7 +792,10 @@ struct FusedGeometry {
 // in 16-bit types, where the wave-per-row kernel (8 packs per lane) was
 // slower. Other rows up to 512 packs keep one row per workgroup, 1 pack per
 // lane (4 rows per iteration measured 3-5 % slower at 448 packs). Wider
-// rows: 2 packs per lane up to 1024, then ceil(ppr / 256) up to kMaxPPT. Three row
+// rows: 2 packs per lane up to 1024, then ceil(ppr / 256) up to kMaxPPT;
+// rows of exactly 1024 packs (hidden 8192 in 16-bit types, 4096 in fp32)
+// take 256 lanes x 4 packs in the pipelined full-row variant instead, 1.5-2 %
+// faster than 512 x 2 (and 8 x 128 was 1-5 % slower). Three row
 // widths would get workgroups of 5 or 6 waves, which a CU's four SIMDs share
 // unequally; they take 64 or 128 lanes with 3 or 5 packs each instead (the
 // pipelined full-row variant): rows of 320, 384 and 640 packs (hidden 2560,
@@ -818,6 +822,8 @@ FusedGeometry fused_geometry(int ppr, bool few_rows)
         }
         if (ppr == kRowsMaxPacks)
             return FusedGeometry{1, ppr, kRowsMaxPacks, 2};
+        if (ppr == 1024)
+            return FusedGeometry{4, 256, 256};
     }
     if (few_rows && ppr > 512 && ppr <= kLatencyMaxPPT * kFusedMaxThreads) {
         k = (ppr + kFusedMaxThreads - 1) / kFusedMaxThreads;
@@ -969,12 +975,13 @@ void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int de
 
 // The pipelined full-row variant runs where it was measured faster: the
 // narrow layouts of 64 or 128 lanes with 3 or 5 packs per lane (rows of 320,
-// 384 and 640 packs, 3-9 % faster), and 256 lanes with 5..8 packs per lane
-// (rows of 1280, 1536, 1792 and 2048 packs: hidden 10240..16384 in 16-bit
-// types, 4-13 % faster than one round trip per slot). With one or two slots
-// on 512 lanes (rows of 512 and 1024 packs) it was as fast or up to 7 %
-// slower: two slots' loads in flight per lane cost more there than the
-// overlap gains.
+// 384 and 640 packs, 3-9 % faster), and 256 lanes with 4..8 packs per lane
+// (rows of 1024, 1280, 1536, 1792 and 2048 packs: hidden 8192..16384 in
+// 16-bit types, 2-13 % faster than 2 x 512 or one round trip per slot). With
+// one or two slots on 512 lanes (rows of 512 and 1024 packs) it was as fast
+// or up to 7 % slower: two slots' loads in flight per lane cost more there
+// than the overlap gains; 3 x 256 (rows of 768 packs) was 2.5 % slower than
+// 2 x 384.
 // Returns false, launching nothing, if the shape does not fit the instance: a
 // workgroup larger than the launch bound would index `part` past its end and
 // exceed the registers the kernel was compiled for, and lanes must cover the row.

@@ -223,9 +223,9 @@ def test_fused_widths_at_the_layout_switch(dtype, hidden):
     and 256 packs (8 or 4 rows per workgroup; the last group may be short),
     the multi-row kernel for rows of 512 packs (2 rows per iteration),
     64 or 128 lanes in the pipelined full-row variant for rows of 320, 384 and
-    640 packs, 256 lanes with 5..8 packs in the same variant for rows of 1280,
-    1536, 1792 and 2048 packs, and up to 512 lanes with 1..8 packs per lane for
-    the rest. The row count at the switch and one past it."""
+    640 packs, 256 lanes with 4..8 packs in the same variant for rows of 1024,
+    1280, 1536, 1792 and 2048 packs, and up to 512 lanes with 1..8 packs per
+    lane for the rest. The row count at the switch and one past it."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for rows in (cus, cus + 1):
         note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
