@@ -78,8 +78,8 @@ constexpr int kSumThreads = AR_SUM_THREADS;
 // CUs): a row of up to 1024 packs takes 1 or 2 packs per lane on up to 512
 // lanes; wider rows (up to 2048 packs) take 3..8 packs per lane on up to 256
 // lanes, which keeps every variant within the VGPR budget of its launch bound
-// (those that fill every slot of every lane - 5..8 x 256 - run pipelined, and
-// so do rows of exactly 1024 packs, as 4 x 256);
+// (those on 256 lanes run pipelined, the last slot possibly partial, and so
+// do rows of exactly 1024 packs, as 4 x 256);
 // rows of 320, 384 and 640 packs take 64 or 128 lanes (see fused_geometry).
 // Latency layout (no more rows than CUs, rows of 513..2048 packs): up to 1024
 // lanes, so each lane's packs - and so the memory round trips of a row - are
@@ -413,15 +413,19 @@ __device__ __forceinline__ void load_slot(const FusedArgs &a, size_t j, u32x4 (&
 // l+(PPT-1)T of the row (T = workgroup size), so each load instruction of a
 // wave covers 1 KiB contiguous. The rounded S stays in registers as packs
 // (4 VGPRs per pack) and the weight packs are loaded before the barrier.
-// FULL: the row fills every slot of every lane (ppr == PPT * T). The slots
-// then need no bounds test and are software-pipelined two deep: slot p+1's
-// loads are issued before slot p's sums, and a compiler fence after each slot
-// keeps later slots' loads from being hoisted further (which would hold every
-// slot's loads in registers). The S stores wait until the last slot: a store
-// between two slots would order the next slot's loads after it (S may be a
-// partial or the residual, so the compiler must assume they overlap). Every
-// element is still read before its own S is written.
-template <class E, int R, int PPT, int BOUND, bool FULL>
+// MODE kFull: the row fills every slot of every lane (ppr == PPT * T). The
+// slots then need no bounds test and are software-pipelined two deep: slot
+// p+1's loads are issued before slot p's sums, and a compiler fence after
+// each slot keeps later slots' loads from being hoisted further (which would
+// hold every slot's loads in registers). The S stores wait until the last
+// slot: a store between two slots would order the next slot's loads after it
+// (S may be a partial or the residual, so the compiler must assume they
+// overlap). Every element is still read before its own S is written.
+// MODE kRagged: the same pipeline when every slot but the last is full
+// ((PPT - 1) * T < ppr < PPT * T); the last slot's loads, sums and stores are
+// done by the lanes it covers. MODE kPlain: one bounds-tested slot at a time.
+constexpr int kPlain = 0, kFull = 1, kRagged = 2;
+template <class E, int R, int PPT, int BOUND, int MODE>
 __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
 {
     __shared__ float part[BOUND / kWave];
@@ -433,23 +437,28 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
         const size_t row0 = row * static_cast<size_t>(a.ppr);
         u32x4 sp[PPT], w[PPT];
         float ss = 0.0f;
-        if (FULL) {
+        if (MODE != kPlain) {
+            // this lane has a pack in the last slot
+            const bool last_ok = MODE == kFull || threadIdx.x + (PPT - 1) * T < a.ppr;
             u32x4 v[2][R], rq[2];
             load_slot<R>(a, row0 + threadIdx.x, v[0], rq[0]);
 #pragma unroll
             for (int p = 0; p < PPT; ++p) {
                 const int j = threadIdx.x + p * T;
-                if (p + 1 < PPT)
+                if (p + 2 < PPT || (p + 1 < PPT && last_ok))
                     load_slot<R>(a, row0 + j + T, v[(p + 1) & 1], rq[(p + 1) & 1]);
-                const u32x4 bq = bias ? bias[j] : u32x4{0, 0, 0, 0};
-                w[p] = weight[j];
-                sp[p] = fused_pre_norm<E, R>(v[p & 1], bias != nullptr, bq, a.residual != nullptr, rq[p & 1]);
-                ss += sum_squares<E>(sp[p]);
+                if (p + 1 < PPT || last_ok) {
+                    const u32x4 bq = bias ? bias[j] : u32x4{0, 0, 0, 0};
+                    w[p] = weight[j];
+                    sp[p] = fused_pre_norm<E, R>(v[p & 1], bias != nullptr, bq, a.residual != nullptr, rq[p & 1]);
+                    ss += sum_squares<E>(sp[p]);
+                }
                 asm volatile("" ::: "memory");
             }
 #pragma unroll
             for (int p = 0; p < PPT; ++p)
-                st16(static_cast<u32x4 *>(a.inter) + row0 + threadIdx.x + p * T, sp[p]);
+                if (p + 1 < PPT || last_ok)
+                    st16(static_cast<u32x4 *>(a.inter) + row0 + threadIdx.x + p * T, sp[p]);
         } else {
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
@@ -477,7 +486,7 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int j = threadIdx.x + p * T;
-            if (FULL || j < a.ppr)
+            if (MODE == kFull || j < a.ppr)
                 st16(static_cast<u32x4 *>(a.out) + row0 + j, normed_pack<E>(sp[p], rstd, w[p]));
         }
         __syncthreads();  // `part` is rewritten by the next row
@@ -962,15 +971,15 @@ int resident_per_cu(K kernel, int threads, int dev, OccCache &cache)
 // The register-row kernel runs as one resident wave of workgroups (CUs x
 // workgroups per CU) that loop over the rows: no second dispatch round, whose
 // refill leaves CUs idle.
-template <class E, int R, int PPT, int BOUND, bool FULL>
+template <class E, int R, int PPT, int BOUND, int MODE>
 void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
 {
     static OccCache occ;
     const size_t resident = static_cast<size_t>(cus) *
-                            resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, FULL>, threads, dev, occ);
+                            resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, MODE>, threads, dev, occ);
     if (grid > resident)
         grid = static_cast<unsigned>(resident);
-    hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, FULL>), dim3(grid), dim3(threads), 0, stream, a);
+    hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, MODE>), dim3(grid), dim3(threads), 0, stream, a);
 }
 
 // The pipelined full-row variant runs where it was measured faster: the
@@ -981,7 +990,11 @@ void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int de
 // one or two slots on 512 lanes (rows of 512 and 1024 packs) it was as fast
 // or up to 7 % slower: two slots' loads in flight per lane cost more there
 // than the overlap gains; 3 x 256 (rows of 768 packs) was 2.5 % slower than
-// 2 x 384.
+// 2 x 384. Rows of 1025..2047 packs that are not a multiple of 256 take the
+// ragged form on 256 lanes (the last slot partly covered): 2-10 % faster than
+// one round trip per slot at hidden 9216 and 13312 in 16-bit types. Forcing
+// 3 x 256 ragged onto rows of 640 packs was 2 % slower than 5 x 128, and
+// 4 x 256 ragged on rows of 896 packs within 1 % of 2 x 448.
 // Returns false, launching nothing, if the shape does not fit the instance: a
 // workgroup larger than the launch bound would index `part` past its end and
 // exceed the registers the kernel was compiled for, and lanes must cover the row.
@@ -992,11 +1005,15 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
         return false;
     if constexpr (PPT >= 3 && PPT <= kFullMaxPPT) {
         if (threads <= kFullLanes && a.ppr == PPT * threads) {
-            launch_fused_pack_as<E, R, PPT, BOUND, true>(a, grid, threads, dev, cus, stream);
+            launch_fused_pack_as<E, R, PPT, BOUND, kFull>(a, grid, threads, dev, cus, stream);
+            return true;
+        }
+        if (threads == kFullLanes && a.ppr > (PPT - 1) * threads) {
+            launch_fused_pack_as<E, R, PPT, BOUND, kRagged>(a, grid, threads, dev, cus, stream);
             return true;
         }
     }
-    launch_fused_pack_as<E, R, PPT, BOUND, false>(a, grid, threads, dev, cus, stream);
+    launch_fused_pack_as<E, R, PPT, BOUND, kPlain>(a, grid, threads, dev, cus, stream);
     return true;
 }
 

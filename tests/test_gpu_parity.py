@@ -215,8 +215,8 @@ def test_fused_widths(dtype, hidden):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [8, 64, 512, 1000, 1024, 2000, 2048, 2560, 3072, 3584, 4096, 5120, 6144, 7168,
-                                    8192, 10240, 12288, 14336, 16384])
+@pytest.mark.parametrize("hidden", [8, 64, 512, 1000, 1024, 2000, 2048, 2560, 3072, 3584, 4096, 4100, 5120, 6144,
+                                    6500, 7168, 8192, 8200, 9216, 10240, 12288, 13312, 14336, 16376, 16384])
 def test_fused_widths_at_the_layout_switch(dtype, hidden):
     """Up to one row per CU the register-row kernel takes its latency layout
     (up to 1024 lanes a row). With more rows: one wave per row for rows of 128
@@ -224,8 +224,10 @@ def test_fused_widths_at_the_layout_switch(dtype, hidden):
     the multi-row kernel for rows of 512 packs (2 rows per iteration),
     64 or 128 lanes in the pipelined full-row variant for rows of 320, 384 and
     640 packs, 256 lanes with 4..8 packs in the same variant for rows of 1024,
-    1280, 1536, 1792 and 2048 packs, and up to 512 lanes with 1..8 packs per
-    lane for the rest. The row count at the switch and one past it."""
+    1280, 1536, 1792 and 2048 packs, and in its ragged form (last slot partly
+    covered, down to one lane: 1025 and 2047 packs) for the other rows of
+    1025..2047 packs, and up to 512 lanes with 1..8 packs per lane for the
+    rest. The row count at the switch and one past it."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for rows in (cus, cus + 1):
         note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
@@ -269,11 +271,11 @@ def test_fused_aliasing(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [512, 1024, 2048, 2560, 3072, 4096, 5120, 8192, 10240, 16384])
+@pytest.mark.parametrize("hidden", [512, 1024, 2048, 2560, 3072, 4096, 5120, 8192, 9216, 10240, 16384])
 def test_fused_aliasing_in_the_throughput_layouts(dtype, hidden):
     """More rows than CUs (the wave-per-row and multi-row kernels, the full-row
     variant whose S stores come after all of a row's loads - on 64, 128 and
-    256 lanes - and the plain slots):
+    256 lanes, and ragged - and the plain slots):
     intermediate == residual and output == a partial still give the oracle's
     results."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
