@@ -79,7 +79,8 @@ constexpr int kSumThreads = AR_SUM_THREADS;
 // lanes; wider rows (up to 2048 packs) take 3..8 packs per lane on up to 256
 // lanes, which keeps every variant within the VGPR budget of its launch bound
 // (those on 256 lanes run pipelined, the last slot possibly partial, and so
-// do rows of exactly 1024 packs, as 4 x 256);
+// do rows of exactly 1024 packs, as 4 x 256); rows of 2049..4096 packs in
+// 16-bit types take 5..8 pipelined packs per lane on 512 lanes;
 // rows of 320, 384 and 640 packs take 64 or 128 lanes (see fused_geometry).
 // Latency layout (no more rows than CUs, rows of 513..2048 packs): up to 1024
 // lanes, so each lane's packs - and so the memory round trips of a row - are
@@ -90,6 +91,7 @@ constexpr int kLatencyMaxPPT = 2;
 constexpr int kFullMaxPPT = 8;   // full-row variant: slots per lane, at most
 constexpr int kFullLanes = 256;  // full-row variant: workgroup size, at most
 constexpr int kRowsMaxPacks = 512;  // multi-row kernel: widest row, and workgroup size bound
+constexpr int kWideRowLanes = 512;  // register path for rows of 2049..4096 packs (16-bit types)
 constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
 constexpr int kElemThreads = 256;       // element-wise kernels
 constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
@@ -812,12 +814,17 @@ struct FusedGeometry {
 // (6 waves of 2 packs) gained at most 2 % and rows of 896 (7 waves) lost on
 // 128 lanes, so they keep the default. Rows of 1280, 1536, 1792 and 2048
 // packs fill 5..8 packs on 256 lanes exactly and so run pipelined too.
+// Rows of 2049..4096 packs in 16-bit types (`wide_rows_in_registers`) take
+// 512 lanes x ceil(ppr / 512) packs, pipelined; wider rows, and fp32 rows
+// past 2048 packs, take the two-pass wide kernel.
 // Latency layout (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024)
 // packs per lane, up to kLatencyMaxPPT.
-FusedGeometry fused_geometry(int ppr, bool few_rows)
+FusedGeometry fused_geometry(int ppr, bool few_rows, bool wide_rows_in_registers)
 {
     int k, bound;
     if (!few_rows) {
+        if (wide_rows_in_registers && ppr > kMaxPPT * 256 && ppr <= kMaxPPT * kWideRowLanes)
+            return FusedGeometry{(ppr + kWideRowLanes - 1) / kWideRowLanes, kWideRowLanes, kWideRowLanes};
         switch (ppr) {
         case 320: return FusedGeometry{5, 64, 256};
         case 384: return FusedGeometry{3, 128, 256};
@@ -1017,6 +1024,26 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
     return true;
 }
 
+// Rows of 2049..4096 packs in 16-bit types: 512 lanes x PPT (5..8) packs in the
+// pipelined variant, full or ragged (one workgroup per CU: up to 221 VGPRs).
+// Against the two-pass wide kernel this measured 15-18 % faster on hidden
+// 18432..32768 (bf16, 8 ranks) and 2.4 % on fp16 2-rank rows of 32768. Only
+// these two forms are instantiated at this bound; fp32 rows of this width
+// keep the wide kernel (its instances here would spill).
+// Returns false, launching nothing, unless the row needs exactly PPT slots of
+// kWideRowLanes lanes.
+template <class E, int R, int PPT>
+bool launch_fused_pack_wide(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
+{
+    if (threads != kWideRowLanes || a.ppr > PPT * threads || a.ppr <= (PPT - 1) * threads)
+        return false;
+    if (a.ppr == PPT * threads)
+        launch_fused_pack_as<E, R, PPT, kWideRowLanes, kFull>(a, grid, threads, dev, cus, stream);
+    else
+        launch_fused_pack_as<E, R, PPT, kWideRowLanes, kRagged>(a, grid, threads, dev, cus, stream);
+    return true;
+}
+
 // Wave-per-row kernel on a resident grid (no more workgroups than row groups).
 // Returns false, launching nothing, unless the row is exactly SL packs per lane.
 template <class E, int R, int SL, int W>
@@ -1071,7 +1098,7 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
         a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
         dev = current_device();
         cus = device_cus(dev);
-        g = fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus));
+        g = fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus), E::kSize == 2);
     }
     if (vec && g.waves > 0) {
         if (log_enabled())
@@ -1112,6 +1139,16 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
             case 1: ok = launch_fused_pack<E, R, 1, kFusedMaxThreads>(a, grid, t, dev, cus, stream); break;
             case 2: ok = launch_fused_pack<E, R, 2, kFusedMaxThreads>(a, grid, t, dev, cus, stream); break;
             default: break;
+            }
+        } else if (g.bound == kWideRowLanes && g.ppt > 2) {
+            if constexpr (E::kSize == 2) {
+                switch (g.ppt) {
+                case 5: ok = launch_fused_pack_wide<E, R, 5>(a, grid, t, dev, cus, stream); break;
+                case 6: ok = launch_fused_pack_wide<E, R, 6>(a, grid, t, dev, cus, stream); break;
+                case 7: ok = launch_fused_pack_wide<E, R, 7>(a, grid, t, dev, cus, stream); break;
+                case 8: ok = launch_fused_pack_wide<E, R, 8>(a, grid, t, dev, cus, stream); break;
+                default: break;
+                }
             }
         } else {
             switch (g.ppt) {

@@ -216,7 +216,8 @@ def test_fused_widths(dtype, hidden):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("hidden", [8, 64, 512, 1000, 1024, 2000, 2048, 2560, 3072, 3584, 4096, 4100, 5120, 6144,
-                                    6500, 7168, 8192, 8200, 9216, 10240, 12288, 13312, 14336, 16376, 16384])
+                                    6500, 7168, 8192, 8200, 9216, 10240, 12288, 13312, 14336, 16376, 16384,
+                                    16392, 18432, 20480, 24576, 28672, 32760, 32768, 32776])
 def test_fused_widths_at_the_layout_switch(dtype, hidden):
     """Up to one row per CU the register-row kernel takes its latency layout
     (up to 1024 lanes a row). With more rows: one wave per row for rows of 128
@@ -226,8 +227,11 @@ def test_fused_widths_at_the_layout_switch(dtype, hidden):
     640 packs, 256 lanes with 4..8 packs in the same variant for rows of 1024,
     1280, 1536, 1792 and 2048 packs, and in its ragged form (last slot partly
     covered, down to one lane: 1025 and 2047 packs) for the other rows of
-    1025..2047 packs, and up to 512 lanes with 1..8 packs per lane for the
-    rest. The row count at the switch and one past it."""
+    1025..2047 packs, 512 lanes with 5..8 packs (full or ragged) for rows of
+    2049..4096 packs in 16-bit types, up to 512 lanes with 1..8 packs per
+    lane for the rest, and the two-pass wide kernel past that (fp32 rows of
+    more than 2048 packs, 16-bit rows of more than 4096). The row count at the
+    switch and one past it."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for rows in (cus, cus + 1):
         note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
@@ -271,7 +275,8 @@ def test_fused_aliasing(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("hidden", [512, 1024, 2048, 2560, 3072, 4096, 5120, 8192, 9216, 10240, 16384])
+@pytest.mark.parametrize("hidden", [512, 1024, 2048, 2560, 3072, 4096, 5120, 8192, 9216, 10240, 16384, 18432,
+                                    32768])
 def test_fused_aliasing_in_the_throughput_layouts(dtype, hidden):
     """More rows than CUs (the wave-per-row and multi-row kernels, the full-row
     variant whose S stores come after all of a row's loads - on 64, 128 and
