@@ -56,7 +56,8 @@ def parse():
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for rel in ("tensor_all_reduce_ar_amd/csrc/ar.hip", "include/ar.h"):
+    for rel in ("tensor_all_reduce_ar_amd/csrc/ar.hip", "tensor_all_reduce_ar_amd/csrc/fused_geometry.h",
+                "include/ar.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -46,6 +46,7 @@
 #include <stdlib.h>
 
 #include "ar.h"
+#include "fused_geometry.h"
 
 namespace {
 
@@ -56,7 +57,17 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPackBytes = 16;
-constexpr int kWave = 64;
+using ar_geometry::FusedGeometry;
+using ar_geometry::kFull;
+using ar_geometry::kFullMaxPPT;
+using ar_geometry::kFusedMaxThreads;
+using ar_geometry::kMaxPPT;
+using ar_geometry::kPlain;
+using ar_geometry::kRagged;
+using ar_geometry::kRowsMaxPacks;
+using ar_geometry::kWave;
+using ar_geometry::kWideRowLanes;
+using ar_geometry::kWideThreads;
 // Tuning constants (compile-time; the defaults are the measured best).
 #ifndef AR_SUM_THREADS
 #define AR_SUM_THREADS 512              // workgroup size of the sum kernel
@@ -74,25 +85,6 @@ constexpr int kWave = 64;
 #define AR_NT_STORES 1                  // non-temporal (streaming) stores
 #endif
 constexpr int kSumThreads = AR_SUM_THREADS;
-// Register-row fused kernel, two layouts. Throughput layout (more rows than
-// CUs): a row of up to 1024 packs takes 1 or 2 packs per lane on up to 512
-// lanes; wider rows (up to 2048 packs) take 3..8 packs per lane on up to 256
-// lanes, which keeps every variant within the VGPR budget of its launch bound
-// (those on 256 lanes run pipelined, the last slot possibly partial, and so
-// do rows of exactly 1024 packs, as 4 x 256); rows of 2049..4096 packs in
-// 16-bit types take 5..8 pipelined packs per lane on 512 lanes;
-// rows of 320, 384 and 640 packs take 64 or 128 lanes (see fused_geometry).
-// Latency layout (no more rows than CUs, rows of 513..2048 packs): up to 1024
-// lanes, so each lane's packs - and so the memory round trips of a row - are
-// halved when the chip is not full anyway.
-constexpr int kMaxPPT = 8;
-constexpr int kFusedMaxThreads = 1024;
-constexpr int kLatencyMaxPPT = 2;
-constexpr int kFullMaxPPT = 8;   // full-row variant: slots per lane, at most
-constexpr int kFullLanes = 256;  // full-row variant: workgroup size, at most
-constexpr int kRowsMaxPacks = 512;  // multi-row kernel: widest row, and workgroup size bound
-constexpr int kWideRowLanes = 512;  // register path for rows of 2049..4096 packs (16-bit types)
-constexpr int kWideThreads = 1024;      // workgroup size for rows wider than that
 constexpr int kElemThreads = 256;       // element-wise kernels
 constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
 
@@ -426,7 +418,6 @@ __device__ __forceinline__ void load_slot(const FusedArgs &a, size_t j, u32x4 (&
 // MODE kRagged: the same pipeline when every slot but the last is full
 // ((PPT - 1) * T < ppr < PPT * T); the last slot's loads, sums and stores are
 // done by the lanes it covers. MODE kPlain: one bounds-tested slot at a time.
-constexpr int kPlain = 0, kFull = 1, kRagged = 2;
 template <class E, int R, int PPT, int BOUND, int MODE>
 __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
 {
@@ -786,81 +777,6 @@ bool sum_vector_ok(const ar_params_t *p)
     return true;
 }
 
-// Launch shape of the register-row kernel for a row of `ppr` packs.
-struct FusedGeometry {
-    int ppt;      // packs per lane; 0 = the row is too wide, the wide kernel takes it
-    int threads;  // workgroup size: the fewest whole waves that cover the row
-    int bound;    // launch bound of the kernel instance (512, 256 or 1024)
-    int rows = 1; // rows per workgroup iteration: > 1 selects the multi-row kernel
-    int waves = 0; // > 0 selects the wave-per-row kernel, with this many waves (rows) per workgroup
-};
-
-// Throughput layout: rows of 128 and 256 packs take the wave-per-row kernel
-// (2 or 4 packs per lane, 8 or 4 rows per workgroup, no barrier): measured
-// 5-7 % faster than one workgroup per row on hidden 1024 and 2048 in 16-bit
-// types. Rows of 512 packs take the multi-row kernel (one pack per lane, 2
-// adjacent rows per iteration, one barrier): 1.5-4 % faster on hidden 4096
-// in 16-bit types, where the wave-per-row kernel (8 packs per lane) was
-// slower. Other rows up to 512 packs keep one row per workgroup, 1 pack per
-// lane (4 rows per iteration measured 3-5 % slower at 448 packs). Wider
-// rows: 2 packs per lane up to 1024, then ceil(ppr / 256) up to kMaxPPT;
-// rows of exactly 1024 packs (hidden 8192 in 16-bit types, 4096 in fp32)
-// take 256 lanes x 4 packs in the pipelined full-row variant instead, 1.5-2 %
-// faster than 512 x 2 (and 8 x 128 was 1-5 % slower). Three row
-// widths would get workgroups of 5 or 6 waves, which a CU's four SIMDs share
-// unequally; they take 64 or 128 lanes with 3 or 5 packs each instead (the
-// pipelined full-row variant): rows of 320, 384 and 640 packs (hidden 2560,
-// 3072 and 5120 in 16-bit types) measured 3-9 % faster so. Rows of 768 packs
-// (6 waves of 2 packs) gained at most 2 % and rows of 896 (7 waves) lost on
-// 128 lanes, so they keep the default. Rows of 1280, 1536, 1792 and 2048
-// packs fill 5..8 packs on 256 lanes exactly and so run pipelined too.
-// Rows of 2049..4096 packs in 16-bit types (`wide_rows_in_registers`) take
-// 512 lanes x ceil(ppr / 512) packs, pipelined; wider rows, and fp32 rows
-// past 2048 packs, take the two-pass wide kernel.
-// Latency layout (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024)
-// packs per lane, up to kLatencyMaxPPT.
-FusedGeometry fused_geometry(int ppr, bool few_rows, bool wide_rows_in_registers)
-{
-    int k, bound;
-    if (!few_rows) {
-        if (wide_rows_in_registers && ppr > kMaxPPT * 256 && ppr <= kMaxPPT * kWideRowLanes)
-            return FusedGeometry{(ppr + kWideRowLanes - 1) / kWideRowLanes, kWideRowLanes, kWideRowLanes};
-        switch (ppr) {
-        case 320: return FusedGeometry{5, 64, 256};
-        case 384: return FusedGeometry{3, 128, 256};
-        case 640: return FusedGeometry{5, 128, 256};
-        default: break;
-        }
-        if (ppr == 128 || ppr == 256) {
-            FusedGeometry g{ppr / kWave, ppr == 128 ? 8 * kWave : 4 * kWave, 512};
-            g.waves = g.threads / kWave;
-            return g;
-        }
-        if (ppr == kRowsMaxPacks)
-            return FusedGeometry{1, ppr, kRowsMaxPacks, 2};
-        if (ppr == 1024)
-            return FusedGeometry{4, 256, 256};
-    }
-    if (few_rows && ppr > 512 && ppr <= kLatencyMaxPPT * kFusedMaxThreads) {
-        k = (ppr + kFusedMaxThreads - 1) / kFusedMaxThreads;
-        bound = kFusedMaxThreads;
-    } else if (ppr <= 512) {
-        k = 1;
-        bound = 512;
-    } else if (ppr <= 1024) {
-        k = 2;
-        bound = 512;
-    } else {
-        k = (ppr + 255) / 256;
-        bound = 256;
-    }
-    if (k > kMaxPPT)
-        return FusedGeometry{0, kWideThreads, kWideThreads};
-    int t = (ppr + k - 1) / k;
-    t = (t + kWave - 1) / kWave * kWave;
-    return FusedGeometry{k, t < kWave ? kWave : t, bound};
-}
-
 // The fused op can take the 16-byte pack kernels: row bytes a multiple of 16
 // and every buffer 16-byte aligned.
 bool fused_vector_ok(const ar_params_t *p)
@@ -1011,13 +927,10 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
     if (threads < kWave || threads > BOUND || threads % kWave != 0 || PPT * threads < a.ppr)
         return false;
     if constexpr (PPT >= 3 && PPT <= kFullMaxPPT) {
-        if (threads <= kFullLanes && a.ppr == PPT * threads) {
-            launch_fused_pack_as<E, R, PPT, BOUND, kFull>(a, grid, threads, dev, cus, stream);
-            return true;
-        }
-        if (threads == kFullLanes && a.ppr > (PPT - 1) * threads) {
-            launch_fused_pack_as<E, R, PPT, BOUND, kRagged>(a, grid, threads, dev, cus, stream);
-            return true;
+        switch (ar_geometry::pipeline_mode(PPT, threads, a.ppr)) {
+        case kFull: launch_fused_pack_as<E, R, PPT, BOUND, kFull>(a, grid, threads, dev, cus, stream); return true;
+        case kRagged: launch_fused_pack_as<E, R, PPT, BOUND, kRagged>(a, grid, threads, dev, cus, stream); return true;
+        default: break;
         }
     }
     launch_fused_pack_as<E, R, PPT, BOUND, kPlain>(a, grid, threads, dev, cus, stream);
@@ -1035,13 +948,13 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
 template <class E, int R, int PPT>
 bool launch_fused_pack_wide(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
 {
-    if (threads != kWideRowLanes || a.ppr > PPT * threads || a.ppr <= (PPT - 1) * threads)
+    if (threads != kWideRowLanes)
         return false;
-    if (a.ppr == PPT * threads)
-        launch_fused_pack_as<E, R, PPT, kWideRowLanes, kFull>(a, grid, threads, dev, cus, stream);
-    else
-        launch_fused_pack_as<E, R, PPT, kWideRowLanes, kRagged>(a, grid, threads, dev, cus, stream);
-    return true;
+    switch (ar_geometry::pipeline_mode(PPT, threads, a.ppr)) {
+    case kFull: launch_fused_pack_as<E, R, PPT, kWideRowLanes, kFull>(a, grid, threads, dev, cus, stream); return true;
+    case kRagged: launch_fused_pack_as<E, R, PPT, kWideRowLanes, kRagged>(a, grid, threads, dev, cus, stream); return true;
+    default: return false;
+    }
 }
 
 // Wave-per-row kernel on a resident grid (no more workgroups than row groups).
@@ -1098,7 +1011,7 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
         a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
         dev = current_device();
         cus = device_cus(dev);
-        g = fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus), E::kSize == 2);
+        g = ar_geometry::fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus), E::kSize == 2);
     }
     if (vec && g.waves > 0) {
         if (log_enabled())
