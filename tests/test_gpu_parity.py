@@ -260,6 +260,35 @@ def test_fused_optional_terms(dtype, bias, residual):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("bias,residual", [(False, False), (True, False), (False, True)])
+def test_fused_optional_terms_in_the_throughput_layouts(dtype, bias, residual):
+    """More rows than CUs, so every register-row layout runs: the wave-per-row
+    kernel (1024), the multi-row kernel (4096), the pipelined variant full on
+    128 and 256 lanes (5120, 8192) and ragged on 256 lanes (9216), the
+    512-lane register path in 16-bit types, ragged (18440), and the plain
+    slots (6144) - each without bias, without residual, or without both."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for hidden in (1024, 4096, 5120, 6144, 8192, 9216, 18440):
+        note(f"[parity] fused {dtype} bias={bias} residual={residual} H={hidden} rows={cus + 2}")
+        w = inputs.random_fused(dtype, 3, cus + 2, hidden, 610, bias=bias, residual=residual)
+        got_out, got_inter = run_fused(w)
+        check_fused(w, got_out, got_inter)
+
+
+@pytest.mark.parametrize("ranks", range(1, 9))
+def test_fused_ranks_in_the_pipelined_layouts(ranks):
+    """Every rank count through the pipelined slot walks: full on 256 lanes
+    (8192), ragged on 256 lanes (9216), and on 512 lanes full and ragged
+    (20480, 20488), bf16, more rows than CUs."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for hidden in (8192, 9216, 20480, 20488):
+        note(f"[parity] fused bf16 R={ranks} H={hidden} rows={cus + 1}")
+        w = inputs.random_fused("bf16", ranks, cus + 1, hidden, 650 + ranks)
+        got_out, got_inter = run_fused(w)
+        check_fused(w, got_out, got_inter)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_fused_aliasing(dtype):
     """intermediate == residual (S replaces the residual in place), and
     output == a partial."""
