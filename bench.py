@@ -247,16 +247,40 @@ def bench_slice(torch, ar, w, args, stream, num):
         sets.append(([p.clone() for p in base], res0.clone() if res0 is not None else None,
                      torch.empty_like(base[0]), torch.empty_like(base[0])))
 
-    def launch(k):
+    def launch(k, on=None):
         parts, res, out, inter = sets[k]
+        st = on if on is not None else stream
         if w.op == "sum":
-            ar.ar_sum_slice(parts, out, 0, num, stream=stream)
+            ar.ar_sum_slice(parts, out, 0, num, stream=st)
         else:
-            ar.ar_residual_rmsnorm_slice(parts, weight, w.eps, out, inter, 0, num, residual=res, stream=stream)
+            ar.ar_residual_rmsnorm_slice(parts, weight, w.eps, out, inter, 0, num, residual=res, stream=st)
 
     steps = max(5, args.steps // 2)
     ms_step, *_ = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
-    return dict(bytes=nb, elements=m, nsets=nsets, ms_step=ms_step, steps=steps)
+
+    # The same calls replayed from a HIP graph (one call per rotating set),
+    # which takes the host's launch cost out of a call this small.
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for k in range(nsets):
+                launch(k, on=side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(2, steps // nsets)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = a.elapsed_time(b) / (reps * nsets)
+    del g
+    return dict(bytes=nb, elements=m, nsets=nsets, ms_step=ms_step, steps=steps, graph_ms=graph_ms)
 
 
 def small_op_latency(torch, ar, inputs, stream, calls=20, reps=10):
@@ -534,8 +558,11 @@ def main():
             "what": f"slice 0 of {w.ranks} of the fused op (one rank's share of a two-shot split)",
             "elements": sl["elements"], "bytes_per_call": sl["bytes"], "us_per_call": round(sl["ms_step"] * 1e3, 2),
             "gbps": round(sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9, 1),
+            "graph_us_per_call": round(sl["graph_ms"] * 1e3, 2),
+            "graph_gbps": round(sl["bytes"] / (sl["graph_ms"] * 1e-3) / 1e9, 1),
         }
-        print(f"[bench] two-shot share: {sl['ms_step'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+        print(f"[bench] two-shot share: {sl['ms_step'] * 1e3:.1f} us/call eager, {sl['graph_ms'] * 1e3:.1f} us/call "
+              f"from a HIP graph", file=sys.stderr, flush=True)
 
     if not args.no_next:
         sl = bench_fused(torch, ar, w, args, stream, layout="slab")

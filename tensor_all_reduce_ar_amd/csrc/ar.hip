@@ -1011,7 +1011,7 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
         a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
         dev = current_device();
         cus = device_cus(dev);
-        g = ar_geometry::fused_geometry(a.ppr, a.rows <= static_cast<size_t>(cus), E::kSize == 2);
+        g = ar_geometry::fused_geometry(a.ppr, ar_geometry::latency_layout(a.ppr, a.rows, cus), E::kSize == 2);
     }
     if (vec && g.waves > 0) {
         if (log_enabled())

@@ -7,6 +7,8 @@
 #ifndef AR_FUSED_GEOMETRY_H
 #define AR_FUSED_GEOMETRY_H
 
+#include <stddef.h>
+
 namespace ar_geometry {
 
 constexpr int kWave = 64;
@@ -18,7 +20,8 @@ constexpr int kWave = 64;
 // do rows of exactly 1024 packs, as 4 x 256); rows of 2049..4096 packs in
 // 16-bit types take 5..8 pipelined packs per lane on 512 lanes;
 // rows of 320, 384 and 640 packs take 64 or 128 lanes (see fused_geometry).
-// Latency layout (no more rows than CUs, rows of 513..2048 packs): up to 1024
+// Latency layout (no more rows than CUs - for rows of 1024..2048 packs, no
+// more than three quarters of them - and rows of 513..2048 packs): up to 1024
 // lanes, so each lane's packs - and so the memory round trips of a row - are
 // halved when the chip is not full anyway.
 constexpr int kMaxPPT = 8;
@@ -66,16 +69,18 @@ struct FusedGeometry {
 // 128 lanes, so they keep the default. Rows of 1025..2048 packs fill 5..8
 // slots on 256 lanes, all full or all but the last, and so run pipelined too.
 // Rows of 2049..4096 packs in 16-bit types (`wide_rows_in_registers`) take
-// 512 lanes x ceil(ppr / 512) packs, pipelined; wider rows, and fp32 rows
-// past 2048 packs, take the two-pass wide kernel.
+// 512 lanes x ceil(ppr / 512) packs, pipelined, at any row count (replayed
+// from a HIP graph, 5-36 % faster than the two-pass kernel at 16..256 rows of
+// hidden 20480 and 32768); wider rows, and fp32 rows past 2048 packs, take
+// the two-pass wide kernel.
 // Latency layout (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024)
 // packs per lane, up to kLatencyMaxPPT.
 inline FusedGeometry fused_geometry(int ppr, bool few_rows, bool wide_rows_in_registers)
 {
     int k, bound;
+    if (wide_rows_in_registers && ppr > kMaxPPT * 256 && ppr <= kMaxPPT * kWideRowLanes)
+        return FusedGeometry{(ppr + kWideRowLanes - 1) / kWideRowLanes, kWideRowLanes, kWideRowLanes};
     if (!few_rows) {
-        if (wide_rows_in_registers && ppr > kMaxPPT * 256 && ppr <= kMaxPPT * kWideRowLanes)
-            return FusedGeometry{(ppr + kWideRowLanes - 1) / kWideRowLanes, kWideRowLanes, kWideRowLanes};
         switch (ppr) {
         case 320: return FusedGeometry{5, 64, 256};
         case 384: return FusedGeometry{3, 128, 256};
@@ -110,6 +115,21 @@ inline FusedGeometry fused_geometry(int ppr, bool few_rows, bool wide_rows_in_re
     int t = (ppr + k - 1) / k;
     t = (t + kWave - 1) / kWave * kWave;
     return FusedGeometry{k, t < kWave ? kWave : t, bound};
+}
+
+// Whether a call of `rows` rows of `ppr` packs on `cus` compute units takes
+// the latency layout: no more rows than CUs, except that rows of 1024..2048
+// packs take the throughput layout once they exceed three quarters of the
+// CUs (replayed from a HIP graph at 256 CUs: 2-8 % faster at 224 and 256
+// rows of hidden 8192..16384 in 16-bit types and 4096 in fp32, within 2 % at
+// 160 and 192 rows, 4-6 % slower at 16 and 64).
+inline bool latency_layout(int ppr, size_t rows, int cus)
+{
+    if (rows > static_cast<size_t>(cus))
+        return false;
+    if (ppr >= 1024 && ppr <= kMaxPPT * 256 && rows * 4 > static_cast<size_t>(cus) * 3)
+        return false;
+    return true;
 }
 
 // Slot walk of the one-row-per-workgroup kernel for `ppt` packs per lane on

@@ -8,13 +8,16 @@
 // library compiles, and the preconditions of the pipelined slot walks.
 // Prints "ok <shapes checked>" or the first failures, and exits non-zero on
 // any failure.
+#include <cstddef>
 #include <cstdio>
+#include <initializer_list>
 
 #include "fused_geometry.h"
 
 using namespace ar_geometry;
 
 static int failures = 0;
+static const FusedGeometry none{0, 0, 0};
 
 static void fail(const char *what, int ppr, bool few, bool wide, const FusedGeometry &g)
 {
@@ -45,7 +48,7 @@ int main()
             for (int wide = 0; wide < 2; ++wide) {
                 const FusedGeometry g = fused_geometry(ppr, few, wide);
                 ++checked;
-                const bool in_registers = ppr <= kMaxPPT * 256 || (wide && !few && ppr <= kMaxPPT * kWideRowLanes);
+                const bool in_registers = ppr <= kMaxPPT * 256 || (wide && ppr <= kMaxPPT * kWideRowLanes);
                 if (g.ppt == 0) {
                     if (in_registers)
                         fail("wide kernel for a row the register path takes", ppr, few, wide, g);
@@ -83,10 +86,29 @@ int main()
             }
         }
     }
+    // The layout switch: the latency layout only when rows do not outnumber
+    // the CUs, and then at most 1 or 2 packs per lane on up to 1024 lanes, or
+    // rows the register path does not hold, or the 512-lane register path.
+    for (int cus : {80, 104, 256, 304}) {
+        for (int ppr = 1; ppr <= 8192; ppr += (ppr < 2100 ? 1 : 7)) {
+            for (size_t rows : {size_t(1), size_t(cus / 2), size_t(cus * 3 / 4), size_t(cus * 3 / 4 + 1),
+                                size_t(cus), size_t(cus + 1), size_t(1) << 20}) {
+                const bool lat = latency_layout(ppr, rows, cus);
+                if (lat && rows > size_t(cus))
+                    fail("latency layout with more rows than CUs", ppr, true, false, none);
+                for (int wide = 0; wide < 2; ++wide) {
+                    const FusedGeometry g = fused_geometry(ppr, lat, wide);
+                    ++checked;
+                    if (lat && g.ppt > 0 && g.bound != kFusedMaxThreads && g.bound != kWideRowLanes &&
+                        ppr > kRowsMaxPacks)
+                        fail("latency layout on a throughput instance", ppr, lat, wide, g);
+                }
+            }
+        }
+    }
     // The slot walk on its own, for every packs-per-lane count, workgroup size
     // and row it could be asked about: a pipelined walk never leaves a slot
     // other than the last one partial.
-    const FusedGeometry none{0, 0, 0};
     for (int ppt = 1; ppt <= kMaxPPT; ++ppt)
         for (int threads = kWave; threads <= kFusedMaxThreads; threads += kWave)
             for (int ppr = 1; ppr <= ppt * threads; ++ppr) {

@@ -18,4 +18,5 @@ def test_every_row_width_has_a_valid_launch_shape(tmp_path):
     subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Werror", "-I", CSRC, "-o", str(exe), CHECK], check=True)
     res = subprocess.run([str(exe)], capture_output=True, text=True)
     assert res.returncode == 0, res.stdout + res.stderr
-    assert res.stdout.strip() == f"ok {8192 * 4}"
+    assert res.stdout.strip().startswith("ok ")
+    assert int(res.stdout.split()[1]) > 8192 * 4

@@ -202,9 +202,10 @@ def test_sum_deterministic_and_on_a_side_stream():
 @pytest.mark.parametrize("hidden", [8, 64, 520, 4096, 4100, 5120, 8192, 10240, 12288, 14336, 16384, 20480, 65536])
 def test_fused_widths(dtype, hidden):
     """Few rows: the register-row kernel in its latency layout (one pack per
-    lane up to 1024 packs a row, two up to 2048), the wide two-pass vector
-    kernel past 2048 packs, and the element kernel for rows whose byte size is
-    not a multiple of 16 (4100 fp16/bf16)."""
+    lane up to 1024 packs a row, two up to 2048), the 512-lane register path
+    for 16-bit rows of 2049..4096 packs, the wide two-pass vector kernel past
+    that (and past 2048 packs in fp32), and the element kernel for rows whose
+    byte size is not a multiple of 16 (4100 fp16/bf16)."""
     for rows in (1, 7, 33, 64):
         if rows * hidden > 1 << 21:
             continue
@@ -236,6 +237,21 @@ def test_fused_widths_at_the_layout_switch(dtype, hidden):
     for rows in (cus, cus + 1):
         note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
         w = inputs.random_fused(dtype, 8 if hidden >= 8192 else 3, rows, hidden, 350 + rows % 7)
+        got_out, got_inter = run_fused(w)
+        check_fused(w, got_out, got_inter)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("hidden", [4096, 8192, 9216, 16384, 20480])
+def test_fused_rows_at_the_latency_switch(dtype, hidden):
+    """Rows of 1024..2048 packs leave the latency layout once they exceed three
+    quarters of the CUs: the row counts on both sides of that switch (and
+    for 16-bit rows past 2048 packs, which take the 512-lane register path at
+    any row count, the same counts)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for rows in (cus * 3 // 4, cus * 3 // 4 + 1):
+        note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
+        w = inputs.random_fused(dtype, 8, rows, hidden, 380 + rows % 5)
         got_out, got_inter = run_fused(w)
         check_fused(w, got_out, got_inter)
 
