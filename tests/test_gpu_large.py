@@ -135,3 +135,47 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for k, v in bufs.items():
             assert np.array_equal(host_bits(v), eager[k]), f"replay {rep}: {k} differs from the eager result"
+
+
+def test_graph_replay_matches_eager_in_the_throughput_layouts():
+    """More rows than CUs, so the captured calls run the throughput layouts:
+    the wave-per-row kernel (1024), the multi-row kernel (4096), the
+    pipelined walk full on 256 lanes (8192), ragged on 256 lanes (9216) and
+    ragged on 512 lanes (20488). Every replay must match the eager result bit
+    for bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    calls = []
+    for hidden in (1024, 4096, 8192, 9216, 20488):
+        w = inputs.random_fused("bf16", 8, cus + 5, hidden, 1600 + hidden % 97)
+        calls.append(dict(parts=[dev(p, w.dtype) for p in w.partials], weight=dev(w.weight, w.dtype),
+                          bias=dev(w.bias, w.dtype), res=dev(w.residual, w.dtype), eps=w.eps))
+    for c in calls:
+        c["out"], c["inter"] = torch.empty_like(c["parts"][0]), torch.empty_like(c["parts"][0])
+    note(f"[graph] throughput layouts, {cus + 5} rows")
+
+    def work():
+        for c in calls:
+            ar.ar_residual_rmsnorm(c["parts"], c["weight"], c["eps"], c["out"], c["inter"], bias=c["bias"],
+                                   residual=c["res"])
+
+    work()
+    torch.cuda.synchronize()
+    eager = [(host_bits(c["out"]), host_bits(c["inter"])) for c in calls]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(5):
+        for c in calls:
+            c["out"].fill_(float("nan"))  # eager work between replays
+            c["inter"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, c in enumerate(calls):
+            assert np.array_equal(host_bits(c["out"]), eager[i][0]), f"replay {rep}: output {i} differs"
+            assert np.array_equal(host_bits(c["inter"]), eager[i][1]), f"replay {rep}: intermediate {i} differs"
