@@ -202,6 +202,11 @@ def _check(t, name: str, dtype, numel: int, device=None):
 def _stream_handle(stream, device) -> int:
     import torch
     if stream is None:
+        # torch's current stream on `device` as a raw handle; the raw query
+        # skips building a Stream object (about 2 us a call)
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return int(raw(device.index))
         stream = torch.cuda.current_stream(device)
     elif stream.device != device:
         raise ValueError(f"stream is on {stream.device}, the buffers on {device}")
@@ -209,11 +214,16 @@ def _stream_handle(stream, device) -> int:
 
 
 def _run(fn, params, stream, device, slice_args=None) -> None:
-    """Launch on the buffers' device (the library uses the current one)."""
+    """Launch on the buffers' device (the library uses the current one);
+    switches device only when that device is not already current."""
     import torch
-    with torch.cuda.device(device):
+    if device.index == torch.cuda.current_device():
         h = _stream_handle(stream, device)
         st = call(fn, params, h) if slice_args is None else call_slice(fn, params, *slice_args, h)
+    else:
+        with torch.cuda.device(device):
+            h = _stream_handle(stream, device)
+            st = call(fn, params, h) if slice_args is None else call_slice(fn, params, *slice_args, h)
     if st != AR_OK:
         raise ArError(st, fn)
 
