@@ -69,12 +69,6 @@ using ar_geometry::kWave;
 using ar_geometry::kWideRowLanes;
 using ar_geometry::kWideThreads;
 // Tuning constants (compile-time; the defaults are the measured best).
-#ifndef AR_SUM_THREADS
-#define AR_SUM_THREADS 512              // workgroup size of the sum kernel
-#endif
-#ifndef AR_SUM_UNROLL
-#define AR_SUM_UNROLL 2                 // packs per lane per step of the sum
-#endif
 #ifndef AR_SUM_GRID_CAP
 #define AR_SUM_GRID_CAP 0               // 0: one workgroup per step; else at most this many
 #endif
@@ -84,7 +78,6 @@ using ar_geometry::kWideThreads;
 #ifndef AR_NT_STORES
 #define AR_NT_STORES 1                  // non-temporal (streaming) stores
 #endif
-constexpr int kSumThreads = AR_SUM_THREADS;
 constexpr int kElemThreads = 256;       // element-wise kernels
 constexpr unsigned kMaxGrid = 1u << 20; // grid cap; kernels loop beyond it
 
@@ -241,13 +234,25 @@ __device__ __forceinline__ float rank_sum_elem(const SumArgs &a, size_t i)
     return acc;
 }
 
+// Workgroup shape of the sum by rank count: 512 lanes x 2 packs per step up
+// to 5 ranks, 256 lanes x 4 packs from 6 ranks on (both 1024 packs a step).
+// Against 512 x 2, the 256 x 4 shape measured 2.4 % faster at 6 ranks, 2.5 %
+// at 7 and 3.5-4 % at 8 (bf16 and fp32, about 600 MB per call), and equal or
+// slower at 2-5 ranks; 256 x 8 won a further 1.5 % at 8 ranks on
+// power-of-two buffer sizes but lost 2 % at 7 ranks on others.
+template <int R>
+struct SumShape {
+    static constexpr int kThreads = R >= 6 ? 256 : 512;
+    static constexpr int kUnroll = R >= 6 ? 4 : 2;
+};
+
 // Sum over 16-byte packs; every pointer 16-byte aligned. Each step a lane
 // loads U packs of each of the R ranks (all in flight), adds, and stores U
-// packs; the workgroup covers kSumThreads*U consecutive packs, coalesced.
+// packs; the workgroup covers T*U consecutive packs, coalesced.
 // The packs after the last full step, and the n % V elements after the last
 // pack, are done by the last workgroup.
-template <class E, int R, int U>
-__global__ __launch_bounds__(kSumThreads) void ar_sum_pack_kernel(SumArgs a)
+template <class E, int R, int T, int U>
+__global__ __launch_bounds__(T) void ar_sum_pack_kernel(SumArgs a)
 {
     const u32x4 *in[R];
 #pragma unroll
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(kSumThreads) void ar_sum_pack_kernel(SumArgs a)
         in[r] = static_cast<const u32x4 *>(a.in[r]);
     u32x4 *out = static_cast<u32x4 *>(a.out);
 
-    const size_t step = static_cast<size_t>(kSumThreads) * U;
+    const size_t step = static_cast<size_t>(T) * U;
     const size_t nfull = a.npacks / step;
     for (size_t c = blockIdx.x; c < nfull; c += gridDim.x) {
         const size_t base = c * step + threadIdx.x;
@@ -264,17 +269,17 @@ __global__ __launch_bounds__(kSumThreads) void ar_sum_pack_kernel(SumArgs a)
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                v[u][r] = ld16(in[r] + base + static_cast<size_t>(u) * kSumThreads);
+                v[u][r] = ld16(in[r] + base + static_cast<size_t>(u) * T);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float acc[E::V];
             rank_sum_pack<E, R>(v[u], acc);
-            st16(out + base + static_cast<size_t>(u) * kSumThreads, E::narrow(acc));
+            st16(out + base + static_cast<size_t>(u) * T, E::narrow(acc));
         }
     }
 
     if (blockIdx.x == gridDim.x - 1) {
-        for (size_t j = nfull * step + threadIdx.x; j < a.npacks; j += kSumThreads) {
+        for (size_t j = nfull * step + threadIdx.x; j < a.npacks; j += T) {
             u32x4 v[R];
 #pragma unroll
             for (int r = 0; r < R; ++r)
@@ -825,14 +830,14 @@ int32_t launch_sum(const ar_params_t *p, hipStream_t stream, bool vec)
     a.n = p->elts_total;
     if (vec) {
         a.npacks = a.n / E::V;
-        const size_t step = static_cast<size_t>(kSumThreads) * AR_SUM_UNROLL;
+        constexpr int T = SumShape<R>::kThreads, U = SumShape<R>::kUnroll;
+        const size_t step = static_cast<size_t>(T) * U;
         unsigned grid = clamp_grid(a.npacks / step);
         if (AR_SUM_GRID_CAP > 0 && grid > static_cast<unsigned>(AR_SUM_GRID_CAP))
             grid = AR_SUM_GRID_CAP;
         if (log_enabled())
-            fprintf(stderr, "[ar] sum pack R=%d V=%d n=%zu grid=%u block=%d unroll=%d\n", R, E::V, a.n, grid,
-                    kSumThreads, AR_SUM_UNROLL);
-        hipLaunchKernelGGL((ar_sum_pack_kernel<E, R, AR_SUM_UNROLL>), dim3(grid), dim3(kSumThreads), 0, stream, a);
+            fprintf(stderr, "[ar] sum pack R=%d V=%d n=%zu grid=%u block=%d unroll=%d\n", R, E::V, a.n, grid, T, U);
+        hipLaunchKernelGGL((ar_sum_pack_kernel<E, R, T, U>), dim3(grid), dim3(T), 0, stream, a);
     } else {
         const unsigned grid = clamp_grid((a.n + kElemThreads - 1) / kElemThreads);
         if (log_enabled())
