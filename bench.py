@@ -241,7 +241,9 @@ def bench_slice(torch, ar, w, args, stream, num):
         nb = (w.ranks + 1) * m * s
     else:
         nb = (w.ranks + 2 + (w.residual is not None)) * m * s + (1 + (w.bias is not None)) * w.hidden * s
-    nsets = rotation_sets(nb * num, (1 if w.op == "sum" else 2) * w.n * s)
+    # rotate by the bytes the share itself touches (inputs and outputs), so
+    # that its sets, not just the full buffers, exceed the cache as required
+    nsets = rotation_sets(nb, (1 if w.op == "sum" else 2) * m * s)
     sets = [(base, res0, out0, inter0)]
     for k in range(1, nsets):
         sets.append(([p.clone() for p in base], res0.clone() if res0 is not None else None,
