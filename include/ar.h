@@ -53,6 +53,12 @@
  * Errors: every entry point returns AR_OK (0) or a negative AR_ERR_* code and
  * never throws. On a validation error nothing is launched and no output is
  * touched. Validation makes no HIP call, so it works on a host without a GPU.
+ *
+ * Size bound: elts_total * sizeof(T) must fit in size_t, and every buffer's
+ * byte range [ptr, ptr + bytes) (full-size buffers: elts_total elements;
+ * bias and weight: hidden_size elements) must end inside the address space.
+ * A call that breaks either is AR_ERR_SHAPE (no such buffer can exist), so
+ * no size check or aliasing check ever works on a wrapped byte count.
  */
 #ifndef TENSOR_ALL_REDUCE_AR_H
 #define TENSOR_ALL_REDUCE_AR_H
@@ -83,7 +89,9 @@ enum {
     AR_ERR_NULL = -1,   /* a required pointer is NULL                              */
     AR_ERR_RANKS = -2,  /* ranks outside 1..AR_MAX_RANKS                           */
     AR_ERR_DTYPE = -3,  /* dtype is not an ar_dtype_t                              */
-    AR_ERR_SHAPE = -4,  /* hidden_size <= 0, or elts_total % hidden_size != 0      */
+    AR_ERR_SHAPE = -4,  /* hidden_size <= 0, elts_total % hidden_size != 0, or a
+                           buffer size past the size bound above (or an unknown
+                           fusion op where one is asked for)                      */
     AR_ERR_EPS = -5,    /* eps is NaN, infinite or negative                        */
     AR_ERR_ALIAS = -6,  /* an output partly overlaps an input or the other output  */
     AR_ERR_ALIGN = -7,  /* a buffer is not aligned to the element size             */
@@ -211,16 +219,24 @@ size_t ar_workspace_size(const ar_params_t *p);
  * recommendation. The base must be AR_SLOT_ALIGN_BYTES-aligned (hipMalloc and
  * torch allocations are) so that every slot takes the 16-byte vector path.
  * slot_offsets has room for `ranks` entries. Makes no HIP call.
- * Returns AR_OK, AR_ERR_RANKS, AR_ERR_DTYPE or AR_ERR_NULL.
+ * Returns AR_OK, AR_ERR_RANKS, AR_ERR_DTYPE, AR_ERR_NULL, or AR_ERR_SHAPE when
+ * the allocation's size (ranks slots) would not fit size_t; on an error the
+ * outputs are untouched.
  */
 int32_t ar_partials_layout(size_t elts_total, int32_t dtype, int32_t ranks, size_t *slot_offsets,
                            size_t *total_bytes);
 
-/* Static, never-NULL description of a status code (unknown codes included). */
+/* Static, never-NULL description of a status code (unknown codes included).
+ * Errors cross this boundary as int32 status codes, never as exceptions, as in
+ * the plugin's enqueue() on the "All Reduce Plugin" page (declared noexcept,
+ * returning int32_t); this call turns a code into text for the caller's log. */
 const char *ar_status_string(int32_t status);
 
 /* The hipError_t (as int) of the last failed HIP call made by this library on
- * the calling thread, or 0 if none failed. Not reset by later successes. */
+ * the calling thread, or 0 if none failed. Not reset by later successes. The
+ * detail behind AR_ERR_HIP, which keeps the int32-status convention of the
+ * plugin's enqueue() ("All Reduce Plugin") while still naming the runtime's
+ * own error. */
 int32_t ar_last_hip_error(void);
 
 #ifdef __cplusplus

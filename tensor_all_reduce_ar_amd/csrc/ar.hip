@@ -46,6 +46,7 @@
 #include <stdlib.h>
 
 #include "ar.h"
+#include "dispatch_rules.h"
 #include "fused_geometry.h"
 
 namespace {
@@ -679,127 +680,10 @@ bool log_enabled()
     return on;
 }
 
-size_t elem_size(int32_t dtype) { return dtype == AR_FP32 ? 4 : 2; }
-
-bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-// Byte ranges [p, p+n) and [q, q+m) share a byte.
-bool overlap(const void *p, size_t n, const void *q, size_t m)
-{
-    if (!p || !q || !n || !m)
-        return false;
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
-    return a < b + m && b < a + n;
-}
-
-// An output may coincide exactly with a full-size input, not overlap it partly.
-bool bad_alias(const void *out, const void *in, size_t bytes)
-{
-    return in != out && overlap(out, bytes, in, bytes);
-}
-
-int32_t validate_common(const ar_params_t *p)
-{
-    if (!p)
-        return AR_ERR_NULL;
-    if (p->dtype != AR_FP32 && p->dtype != AR_FP16 && p->dtype != AR_BF16)
-        return AR_ERR_DTYPE;
-    if (p->ranks < 1 || p->ranks > AR_MAX_RANKS)
-        return AR_ERR_RANKS;
-    return AR_OK;
-}
-
-int32_t validate_sum(const ar_params_t *p)
-{
-    int32_t st = validate_common(p);
-    if (st != AR_OK || p->elts_total == 0)
-        return st;
-    const size_t s = elem_size(p->dtype), bytes = p->elts_total * s;
-    if (!p->local_output_buffer_ptr)
-        return AR_ERR_NULL;
-    for (int r = 0; r < p->ranks; ++r)
-        if (!p->input_buffer_ptrs[r])
-            return AR_ERR_NULL;
-    if (!aligned(p->local_output_buffer_ptr, s))
-        return AR_ERR_ALIGN;
-    for (int r = 0; r < p->ranks; ++r)
-        if (!aligned(p->input_buffer_ptrs[r], s))
-            return AR_ERR_ALIGN;
-    for (int r = 0; r < p->ranks; ++r)
-        if (bad_alias(p->local_output_buffer_ptr, p->input_buffer_ptrs[r], bytes))
-            return AR_ERR_ALIAS;
-    return AR_OK;
-}
-
-int32_t validate_fused(const ar_params_t *p)
-{
-    int32_t st = validate_common(p);
-    if (st != AR_OK)
-        return st;
-    const ar_fusion_params_t &f = p->fusion_params;
-    if (f.hidden_size <= 0 || p->elts_total % static_cast<size_t>(f.hidden_size) != 0)
-        return AR_ERR_SHAPE;
-    if (!(f.eps >= 0.0f) || isinf(f.eps))
-        return AR_ERR_EPS;
-    if (p->elts_total == 0)
-        return AR_OK;
-    const size_t s = elem_size(p->dtype), bytes = p->elts_total * s;
-    const size_t hbytes = static_cast<size_t>(f.hidden_size) * s;
-    void *out = p->local_output_buffer_ptr, *inter = f.intermediate_buffer;
-    if (!out || !inter || !f.weight_buffer)
-        return AR_ERR_NULL;
-    for (int r = 0; r < p->ranks; ++r)
-        if (!p->input_buffer_ptrs[r])
-            return AR_ERR_NULL;
-    const void *ptrs[] = {out, inter, f.weight_buffer, f.bias_buffer, f.residual_buffer};
-    for (const void *q : ptrs)
-        if (q && !aligned(q, s))
-            return AR_ERR_ALIGN;
-    for (int r = 0; r < p->ranks; ++r)
-        if (!aligned(p->input_buffer_ptrs[r], s))
-            return AR_ERR_ALIGN;
-    if (overlap(out, bytes, inter, bytes))
-        return AR_ERR_ALIAS;
-    for (void *o : {out, inter}) {
-        for (int r = 0; r < p->ranks; ++r)
-            if (bad_alias(o, p->input_buffer_ptrs[r], bytes))
-                return AR_ERR_ALIAS;
-        if (overlap(o, bytes, f.weight_buffer, hbytes) || overlap(o, bytes, f.bias_buffer, hbytes))
-            return AR_ERR_ALIAS;
-    }
-    if (bad_alias(inter, f.residual_buffer, bytes) || bad_alias(out, f.residual_buffer, bytes))
-        return AR_ERR_ALIAS;
-    return AR_OK;
-}
-
-bool sum_vector_ok(const ar_params_t *p)
-{
-    if (!aligned(p->local_output_buffer_ptr, kPackBytes))
-        return false;
-    for (int r = 0; r < p->ranks; ++r)
-        if (!aligned(p->input_buffer_ptrs[r], kPackBytes))
-            return false;
-    return true;
-}
-
-// The fused op can take the 16-byte pack kernels: row bytes a multiple of 16
-// and every buffer 16-byte aligned.
-bool fused_vector_ok(const ar_params_t *p)
-{
-    const ar_fusion_params_t &f = p->fusion_params;
-    const size_t s = elem_size(p->dtype);
-    if ((static_cast<size_t>(f.hidden_size) * s) % kPackBytes != 0)
-        return false;
-    const void *ptrs[] = {p->local_output_buffer_ptr, f.intermediate_buffer, f.weight_buffer, f.bias_buffer,
-                          f.residual_buffer};
-    for (const void *q : ptrs)
-        if (q && !aligned(q, kPackBytes))
-            return false;
-    for (int r = 0; r < p->ranks; ++r)
-        if (!aligned(p->input_buffer_ptrs[r], kPackBytes))
-            return false;
-    return true;
-}
+using ar_host::elem_size;
+using ar_host::fused_vector_ok;
+using ar_host::sliced;
+using ar_host::sum_vector_ok;
 
 int32_t check_launch(const char *what)
 {
@@ -1160,62 +1044,16 @@ int32_t run_fused(const ar_params_t *p, hipStream_t stream)
     return dispatch<FusedLauncher>(p->dtype, p->ranks, p, stream, fused_vector_ok(p));
 }
 
-constexpr int32_t kMaxSlices = 1024;
-
-// Elements [begin, end) of slice `slice` of `num_slices` (two-shot split).
-// Sum: equal shares of ceil(N / S) elements rounded up to whole 16-byte
-// packs, so every slice of a 16-byte-aligned buffer starts 16-byte aligned.
-// Fused: equal shares of ceil(rows / S) whole rows.
-int32_t slice_range(const ar_params_t *p, int32_t fusion_op, int32_t slice, int32_t num_slices, size_t *begin,
-                    size_t *end)
-{
-    if (num_slices < 1 || num_slices > kMaxSlices || slice < 0 || slice >= num_slices)
-        return AR_ERR_SLICE;
-    const size_t S = static_cast<size_t>(num_slices), k = static_cast<size_t>(slice), n = p->elts_total;
-    if (fusion_op == AR_FUSION_NONE) {
-        const size_t unit = kPackBytes / elem_size(p->dtype);
-        const size_t per = ((n + S - 1) / S + unit - 1) / unit * unit;
-        *begin = k * per < n ? k * per : n;
-        *end = *begin + per < n ? *begin + per : n;
-        return AR_OK;
-    }
-    if (fusion_op != AR_FUSION_RESIDUAL_RMS_NORM)
-        return AR_ERR_SHAPE;
-    const size_t H = static_cast<size_t>(p->fusion_params.hidden_size);
-    const size_t rows = n / H, per = (rows + S - 1) / S;
-    const size_t r0 = k * per < rows ? k * per : rows;
-    const size_t r1 = r0 + per < rows ? r0 + per : rows;
-    *begin = r0 * H;
-    *end = r1 * H;
-    return AR_OK;
-}
-
-// Params restricted to elements [begin, end): every full-size buffer is
-// offset; bias and weight ([hidden]) are not.
-ar_params_t sliced(const ar_params_t *p, size_t begin, size_t end)
-{
-    ar_params_t q = *p;
-    const size_t off = begin * elem_size(p->dtype);
-    auto at = [off](const void *b) -> const void * {
-        return b ? static_cast<const void *>(static_cast<const char *>(b) + off) : nullptr;
-    };
-    for (int r = 0; r < p->ranks; ++r)
-        q.input_buffer_ptrs[r] = at(p->input_buffer_ptrs[r]);
-    q.local_output_buffer_ptr = const_cast<void *>(at(p->local_output_buffer_ptr));
-    q.fusion_params.residual_buffer = at(p->fusion_params.residual_buffer);
-    q.fusion_params.intermediate_buffer = const_cast<void *>(at(p->fusion_params.intermediate_buffer));
-    q.elts_total = end - begin;
-    return q;
-}
-
 }  // namespace
 
 // ------------------------------------------------------------------- C ABI
+// Every entry point runs the host rules of dispatch_rules.h first; nothing
+// is launched unless they pass.
 extern "C" {
 
 int32_t ar_sum(const ar_params_t *p, void *hip_stream)
 {
-    int32_t st = validate_sum(p);
+    int32_t st = ar_host::validate_sum(p);
     if (st != AR_OK || p->elts_total == 0)
         return st;
     return run_sum(p, static_cast<hipStream_t>(hip_stream));
@@ -1223,7 +1061,7 @@ int32_t ar_sum(const ar_params_t *p, void *hip_stream)
 
 int32_t ar_residual_rmsnorm(const ar_params_t *p, void *hip_stream)
 {
-    int32_t st = validate_fused(p);
+    int32_t st = ar_host::validate_fused(p);
     if (st != AR_OK || p->elts_total == 0)
         return st;
     return run_fused(p, static_cast<hipStream_t>(hip_stream));
@@ -1231,67 +1069,41 @@ int32_t ar_residual_rmsnorm(const ar_params_t *p, void *hip_stream)
 
 int32_t ar_rmsnorm(const ar_params_t *p, void *hip_stream)
 {
-    if (p && p->ranks != 1)
-        return AR_ERR_RANKS;
-    return ar_residual_rmsnorm(p, hip_stream);
+    int32_t st = ar_host::validate_rmsnorm(p);
+    if (st != AR_OK || p->elts_total == 0)
+        return st;
+    return run_fused(p, static_cast<hipStream_t>(hip_stream));
 }
 
 int32_t ar_slice_range(const ar_params_t *p, int32_t fusion_op, int32_t slice, int32_t num_slices, size_t *begin,
                        size_t *end)
 {
-    if (!begin || !end)
-        return AR_ERR_NULL;
-    int32_t st = fusion_op == AR_FUSION_RESIDUAL_RMS_NORM ? validate_fused(p)
-                 : fusion_op == AR_FUSION_NONE            ? validate_sum(p)
-                                                          : AR_ERR_SHAPE;
-    if (st != AR_OK)
-        return st;
-    return slice_range(p, fusion_op, slice, num_slices, begin, end);
+    return ar_host::slice_range_checked(p, fusion_op, slice, num_slices, begin, end);
 }
 
 int32_t ar_sum_slice(const ar_params_t *p, int32_t slice, int32_t num_slices, void *hip_stream)
 {
-    int32_t st = validate_sum(p);
-    if (st != AR_OK)
-        return st;
     size_t b = 0, e = 0;
-    st = slice_range(p, AR_FUSION_NONE, slice, num_slices, &b, &e);
+    int32_t st = ar_host::slice_range_checked(p, AR_FUSION_NONE, slice, num_slices, &b, &e);
     if (st != AR_OK || b == e)
         return st;
-    const ar_params_t q = sliced(p, b, e);
+    const ar_params_t q = sliced(p, AR_FUSION_NONE, b, e);
     return run_sum(&q, static_cast<hipStream_t>(hip_stream));
 }
 
 int32_t ar_residual_rmsnorm_slice(const ar_params_t *p, int32_t slice, int32_t num_slices, void *hip_stream)
 {
-    int32_t st = validate_fused(p);
-    if (st != AR_OK)
-        return st;
     size_t b = 0, e = 0;
-    st = slice_range(p, AR_FUSION_RESIDUAL_RMS_NORM, slice, num_slices, &b, &e);
+    int32_t st = ar_host::slice_range_checked(p, AR_FUSION_RESIDUAL_RMS_NORM, slice, num_slices, &b, &e);
     if (st != AR_OK || b == e)
         return st;
-    const ar_params_t q = sliced(p, b, e);
+    const ar_params_t q = sliced(p, AR_FUSION_RESIDUAL_RMS_NORM, b, e);
     return run_fused(&q, static_cast<hipStream_t>(hip_stream));
 }
 
 int32_t ar_configuration_supported(const ar_params_t *p, int32_t fusion_op)
 {
-    if (fusion_op == AR_FUSION_NONE) {
-        int32_t st = validate_sum(p);
-        if (st != AR_OK)
-            return st;
-        return (p->elts_total == 0 || p->ranks == 1 || sum_vector_ok(p)) ? 1 : 0;
-    }
-    if (fusion_op == AR_FUSION_RESIDUAL_RMS_NORM) {
-        int32_t st = validate_fused(p);
-        if (st != AR_OK)
-            return st;
-        if (p->elts_total == 0)
-            return 1;
-        return fused_vector_ok(p) ? 1 : 0;
-    }
-    return AR_ERR_SHAPE;
+    return ar_host::configuration_supported(p, fusion_op);
 }
 
 size_t ar_workspace_size(const ar_params_t *p)
@@ -1302,18 +1114,7 @@ size_t ar_workspace_size(const ar_params_t *p)
 
 int32_t ar_partials_layout(size_t elts_total, int32_t dtype, int32_t ranks, size_t *slot_offsets, size_t *total_bytes)
 {
-    if (dtype != AR_FP32 && dtype != AR_FP16 && dtype != AR_BF16)
-        return AR_ERR_DTYPE;
-    if (ranks < 1 || ranks > AR_MAX_RANKS)
-        return AR_ERR_RANKS;
-    if (!slot_offsets || !total_bytes)
-        return AR_ERR_NULL;
-    const size_t a = AR_SLOT_ALIGN_BYTES;
-    const size_t stride = (elts_total * elem_size(dtype) + a - 1) / a * a + AR_SLOT_STAGGER_BYTES;
-    for (int r = 0; r < ranks; ++r)
-        slot_offsets[r] = static_cast<size_t>(r) * stride;
-    *total_bytes = static_cast<size_t>(ranks) * stride;
-    return AR_OK;
+    return ar_host::partials_layout(elts_total, dtype, ranks, slot_offsets, total_bytes);
 }
 
 const char *ar_status_string(int32_t status)
@@ -1323,7 +1124,9 @@ const char *ar_status_string(int32_t status)
     case AR_ERR_NULL: return "AR_ERR_NULL: a required pointer is NULL";
     case AR_ERR_RANKS: return "AR_ERR_RANKS: ranks outside 1..AR_MAX_RANKS";
     case AR_ERR_DTYPE: return "AR_ERR_DTYPE: unknown element type";
-    case AR_ERR_SHAPE: return "AR_ERR_SHAPE: hidden_size <= 0 or elts_total not a multiple of it (or unknown fusion op)";
+    case AR_ERR_SHAPE:
+        return "AR_ERR_SHAPE: hidden_size <= 0, elts_total not a multiple of it, a buffer size that does not fit "
+               "the address space, or an unknown fusion op";
     case AR_ERR_EPS: return "AR_ERR_EPS: eps is NaN, infinite or negative";
     case AR_ERR_ALIAS: return "AR_ERR_ALIAS: an output partly overlaps an input or the other output";
     case AR_ERR_ALIGN: return "AR_ERR_ALIGN: a buffer is not aligned to the element size";

@@ -245,15 +245,79 @@ def test_unknown_fusion_op_rejected():
     assert ar.ar_configuration_supported(sum_params(), 2) < 0
 
 
+def hip_devices_visible() -> bool:
+    """Whether the HIP runtime libar.so links sees a device (asked directly,
+    not through torch, whose device list can differ). Any doubt counts as yes."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        try:
+            hip = ctypes.CDLL("/opt/rocm/lib/libamdhip64.so")
+        except OSError:
+            return True
+    n = ctypes.c_int(0)
+    rc = hip.hipGetDeviceCount(ctypes.byref(n))
+    return rc == 0 and n.value > 0 or rc not in (0, 100)  # 100: hipErrorNoDevice
+
+
+no_hip_device = pytest.mark.skipif(hip_devices_visible(),
+                                   reason="host-only case: a HIP device is visible, and a validation bug here "
+                                          "would launch on made-up addresses")
+
+
+@no_hip_device
 def test_launch_without_a_device_reports_hip_error():
     """Forced from the host: with no GPU present, a valid call reaches the
     launch, which fails; the status is AR_ERR_HIP and nothing is thrown."""
-    import torch
-    if torch.cuda.device_count() > 0:
-        pytest.skip("a GPU is present; this case needs a host without one")
     assert ar.call("ar_sum", sum_params()) == ar.AR_ERR_HIP
     assert ar.ar_last_hip_error() != 0
     assert ar.call("ar_residual_rmsnorm", fused_params()) == ar.AR_ERR_HIP
+
+
+SIZE_MAX = (1 << 64) - 1
+
+
+@no_hip_device
+@pytest.mark.parametrize("n,dtype", [((1 << 62) + 16, ar.AR_FP32), (SIZE_MAX // 2 + 1, ar.AR_FP16),
+                                     (SIZE_MAX // 2 + 1, ar.AR_BF16), (SIZE_MAX // 4 + 1, ar.AR_FP32),
+                                     (SIZE_MAX, ar.AR_BF16)])
+def test_sizes_whose_bytes_wrap_are_rejected_everywhere(n, dtype):
+    """elts_total * sizeof(T) past SIZE_MAX: every entry point returns
+    AR_ERR_SHAPE before any HIP call (the wrapped byte count would otherwise
+    pass every aliasing check and launch over the whole size)."""
+    hidden = 16
+    for ranks in (1, 2, 8):
+        sp = sum_params(n=n, ranks=ranks, dtype=dtype)
+        fp = fused_params(n=n, ranks=ranks, dtype=dtype, hidden=hidden) if n % hidden == 0 else None
+        assert ar.call("ar_sum", sp) == ar.AR_ERR_SHAPE
+        assert sum_status(sp) == ar.AR_ERR_SHAPE
+        assert ar.call_slice("ar_sum_slice", sp, 0, 2) == ar.AR_ERR_SHAPE
+        assert ar.ar_slice_range(sp, ar.AR_FUSION_NONE, 0, 2)[0] == ar.AR_ERR_SHAPE
+        if fp is not None:
+            assert ar.call("ar_residual_rmsnorm", fp) == ar.AR_ERR_SHAPE
+            assert fused_status(fp) == ar.AR_ERR_SHAPE
+            assert ar.call_slice("ar_residual_rmsnorm_slice", fp, 1, 2) == ar.AR_ERR_SHAPE
+            assert ar.ar_slice_range(fp, ar.AR_FUSION_RESIDUAL_RMS_NORM, 0, 2)[0] == ar.AR_ERR_SHAPE
+            if ranks == 1:
+                assert ar.call("ar_rmsnorm", fp) == ar.AR_ERR_SHAPE
+
+
+@no_hip_device
+def test_buffers_past_the_end_of_the_address_space_are_rejected():
+    top = SIZE_MAX & ~255
+    n = 1 << 40  # 2 TiB of fp16: fits size_t, not below `top`
+    assert ar.call("ar_sum", sum_params(n=n, dtype=ar.AR_FP16, out=top - (1 << 38))) == ar.AR_ERR_SHAPE
+    assert ar.call("ar_sum", sum_params(n=n, dtype=ar.AR_FP16, inputs=[A, top - 256])) == ar.AR_ERR_SHAPE
+    assert ar.call("ar_residual_rmsnorm", fused_params(n=n, dtype=ar.AR_FP16, residual=top)) == ar.AR_ERR_SHAPE
+    assert ar.call("ar_residual_rmsnorm", fused_params(n=1 << 20, hidden=1 << 20, weight=top)) == ar.AR_ERR_SHAPE
+
+
+def test_partials_layout_rejects_sizes_that_do_not_fit():
+    assert ar.ar_partials_layout((1 << 62) + 1, ar.AR_FP32, 8)[0] == ar.AR_ERR_SHAPE
+    assert ar.ar_partials_layout(1 << 59, ar.AR_FP32, 8)[0] == ar.AR_ERR_SHAPE   # ranks * stride wraps
+    assert ar.ar_partials_layout(SIZE_MAX // 2, ar.AR_FP16, 1)[0] == ar.AR_ERR_SHAPE  # round-up wraps
+    st, offs, total = ar.ar_partials_layout(1 << 58, ar.AR_FP32, 8)
+    assert st == ar.AR_OK and total == 8 * ((1 << 60) + 4096)
 
 
 def test_product_path_fails_loudly_without_the_library(tmp_path):
