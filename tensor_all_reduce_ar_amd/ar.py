@@ -16,7 +16,9 @@ Entry points, same names as the C ABI:
   ar_slice_range(params, fusion_op, slice_index, num_slices)
   ar_configuration_supported(params, fusion_op), ar_workspace_size(params),
   ar_partials_layout(elts_total, dtype, ranks), ar_status_string(code), ar_last_hip_error()
-plus ``Params`` / ``make_params``, ``call`` and ``call_slice`` for raw-pointer use.
+plus ``allocate_workspace`` (one device allocation holding the R partials at
+the slots ar_partials_layout gives), and ``Params`` / ``make_params``, ``call``
+and ``call_slice`` for raw-pointer use.
 """
 from __future__ import annotations
 
@@ -174,6 +176,42 @@ def ar_partials_layout(elts_total: int, dtype: int, ranks: int):
     total = ctypes.c_size_t(0)
     st = load().ar_partials_layout(elts_total, dtype, ranks, offs if ranks > 0 else None, ctypes.byref(total))
     return st, [offs[r] for r in range(max(0, ranks))] if st == AR_OK else [], total.value
+
+
+class Workspace:
+    """One device allocation holding R partials of ``elts_total`` elements at
+    the slot offsets of ar_partials_layout.
+
+    ``buffer`` is the allocation (uint8, ``total_bytes`` long), ``partials``
+    the R typed 1-D views (one per rank, in rank order), ``offsets`` their
+    byte offsets in it. The views are what the producers of the partials
+    write and what ar_sum / ar_residual_rmsnorm read; they share ``buffer``'s
+    memory, which lives as long as any of them does."""
+
+    def __init__(self, buffer, partials, offsets, total_bytes: int):
+        self.buffer, self.partials, self.offsets, self.total_bytes = buffer, partials, offsets, total_bytes
+
+
+def allocate_workspace(elts_total: int, dtype, ranks: int, device=None) -> Workspace:
+    """Allocate the R partials in one device allocation laid out by
+    ar_partials_layout (the one-GPU counterpart of the comm-buffer workspace
+    that CustomAllReduceHelper sizes and allocates in "allreduce.d2",
+    allocate_workspace(mapping, size): there each rank's buffer is a peer's;
+    here every slot is local). The slots are 256-byte aligned and staggered by
+    4 KiB, which the fused kernel reads faster than separate power-of-two
+    allocations. ``dtype`` is a torch dtype (float32, float16, bfloat16);
+    ``device`` defaults to the current CUDA (HIP) device. The contents are
+    uninitialised. Raises ArError if the layout is rejected."""
+    import torch
+    code = _dtype_code(torch.empty(0, dtype=dtype))
+    st, offs, total = ar_partials_layout(int(elts_total), code, int(ranks))
+    if st != AR_OK:
+        raise ArError(st, "ar_partials_layout")
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    size = torch.empty(0, dtype=dtype).element_size()
+    views = [buf[o:o + int(elts_total) * size].view(dtype) for o in offs]
+    return Workspace(buf, views, offs, total)
 
 
 # ------------------------------------------------------------ torch front end

@@ -241,17 +241,36 @@ __device__ __forceinline__ float rank_sum_elem(const SumArgs &a, size_t i)
 // at 7 and 3.5-4 % at 8 (bf16 and fp32, about 600 MB per call), and equal or
 // slower at 2-5 ranks; 256 x 8 won a further 1.5 % at 8 ranks on
 // power-of-two buffer sizes but lost 2 % at 7 ranks on others.
+// Calls too small to give every CU a 1024-pack step (fewer than
+// kSumSmallPacksPerCU packs per CU) take steps of kSumSmallThreads lanes x 1
+// pack instead, so that the grid still spreads over the whole chip.
 template <int R>
 struct SumShape {
     static constexpr int kThreads = R >= 6 ? 256 : 512;
     static constexpr int kUnroll = R >= 6 ? 4 : 2;
 };
+#ifndef AR_SUM_SMALL_THREADS
+#define AR_SUM_SMALL_THREADS 256
+#endif
+#ifndef AR_SUM_SMALL_UNROLL
+#define AR_SUM_SMALL_UNROLL 1
+#endif
+#ifndef AR_SUM_SMALL_PACKS_PER_CU
+#define AR_SUM_SMALL_PACKS_PER_CU 1024
+#endif
+constexpr int kSumSmallThreads = AR_SUM_SMALL_THREADS;
+constexpr int kSumSmallUnroll = AR_SUM_SMALL_UNROLL;
+constexpr size_t kSumSmallPacksPerCU = AR_SUM_SMALL_PACKS_PER_CU;
 
-// Sum over 16-byte packs; every pointer 16-byte aligned. Each step a lane
+// Sum over 16-byte packs; every pointer 16-byte aligned. The work is cut into
+// units: each full step of T*U consecutive packs is one unit, in which a lane
 // loads U packs of each of the R ranks (all in flight), adds, and stores U
-// packs; the workgroup covers T*U consecutive packs, coalesced.
-// The packs after the last full step, and the n % V elements after the last
-// pack, are done by the last workgroup.
+// packs, coalesced across the workgroup. The packs after the last full step
+// and the n % V elements after the last pack form one more unit of their own,
+// given to a workgroup of its own, so no workgroup does a second round trip
+// for them after its own step. Workgroups loop over the full steps (the grid
+// is capped at kMaxGrid); the remainder code sits after that loop so that it
+// does not add to the step loop's registers.
 template <class E, int R, int T, int U>
 __global__ __launch_bounds__(T) void ar_sum_pack_kernel(SumArgs a)
 {
@@ -279,19 +298,30 @@ __global__ __launch_bounds__(T) void ar_sum_pack_kernel(SumArgs a)
         }
     }
 
-    if (blockIdx.x == gridDim.x - 1) {
-        for (size_t j = nfull * step + threadIdx.x; j < a.npacks; j += T) {
-            u32x4 v[R];
+    // The remainder unit (index nfull): fewer than T*U packs, then the tail
+    // elements. With an uncapped grid its workgroup has no full step.
+    const bool rem = nfull * step < a.npacks || a.npacks * E::V < a.n;
+    if (rem && blockIdx.x == nfull % gridDim.x) {
+        const size_t base = nfull * step + threadIdx.x;
+        u32x4 v[U][R];
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                v[r] = ld16(in[r] + j);
-            float acc[E::V];
-            rank_sum_pack<E, R>(v, acc);
-            st16(out + j, E::narrow(acc));
-        }
+        for (int u = 0; u < U; ++u)
+            if (base + static_cast<size_t>(u) * T < a.npacks)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    v[u][r] = ld16(in[r] + base + static_cast<size_t>(u) * T);
         const size_t i = a.npacks * E::V + threadIdx.x;
-        if (i < a.n)
-            E::store1(a.out, i, rank_sum_elem<E, R>(a, i));
+        const bool tail = i < a.n;
+        const float t = tail ? rank_sum_elem<E, R>(a, i) : 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + static_cast<size_t>(u) * T < a.npacks) {
+                float acc[E::V];
+                rank_sum_pack<E, R>(v[u], acc);
+                st16(out + base + static_cast<size_t>(u) * T, E::narrow(acc));
+            }
+        if (tail)
+            E::store1(a.out, i, t);
     }
 }
 
@@ -317,16 +347,36 @@ struct FusedArgs {
     float eps;
 };
 
+// x + (x moved across lanes by the DPP control `ctrl`), in one VALU op.
+// Lanes of rows outside `row_mask` take 0 as the moved value (x + 0 = x: the
+// sums here are of squares, never -0).
+template <int ctrl, int row_mask>
+__device__ __forceinline__ float dpp_add(float x)
+{
+    const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, row_mask, 0xF, false);
+    return x + __builtin_bit_cast(float, moved);
+}
+
+// Sum of x over the 64 lanes of a wave, the same bits in every lane, with no
+// LDS traffic: DPP lane moves inside each row of 16 lanes (pair swap, quad
+// swap, half-row mirror, row mirror; each step adds two equal-sized groups,
+// a + b in one lane and b + a in its partner, so the row holds one value),
+// then the row broadcasts 15 and 31 fold the four rows into lane 63:
+// (r3 + r2) + (r1 + r0), read back as a wave-uniform scalar. Fixed order, so
+// repeat calls agree bitwise.
 __device__ __forceinline__ float wave_sum(float x)
 {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1)
-        x += __shfl_xor(x, off, kWave);
-    return x;
+    x = dpp_add<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
+    x = dpp_add<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
+    x = dpp_add<0x141, 0xF>(x);  // row_half_mirror
+    x = dpp_add<0x140, 0xF>(x);  // row_mirror
+    x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), kWave - 1));
 }
 
 // Sum of x over the workgroup, the same value in every lane. Fixed order
-// (lanes by xor-butterfly, then waves 0..n-1), so repeat calls agree bitwise.
+// (lanes by wave_sum, then waves 0..n-1), so repeat calls agree bitwise.
 // One barrier; `part` must not be reused before the next barrier.
 __device__ __forceinline__ float block_sum(float x, float *part)
 {
@@ -494,7 +544,7 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
 
 // Fused op for narrow rows of exactly 64 * SL packs when they outnumber the
 // CUs: one wave per row and no barrier at all. The row's sum of squares is
-// reduced inside the wave (xor butterfly), so waves never wait for each other;
+// reduced inside the wave (wave_sum), so waves never wait for each other;
 // a workgroup's W waves take W adjacent rows. Lane l holds packs l + 64 p; the
 // slots are software-pipelined two deep like the full-row variant (next
 // slot's loads before this slot's sums, a compiler fence per slot, S stored
@@ -704,6 +754,22 @@ unsigned clamp_grid(size_t blocks)
     return blocks > kMaxGrid ? kMaxGrid : static_cast<unsigned>(blocks);
 }
 
+template <class E, int R, int T, int U>
+void launch_sum_as(const SumArgs &a, hipStream_t stream)
+{
+    const size_t step = static_cast<size_t>(T) * U, nfull = a.npacks / step;
+    const size_t units = nfull + (nfull * step < a.npacks || a.npacks * E::V < a.n);
+    unsigned grid = clamp_grid(units);
+    if (AR_SUM_GRID_CAP > 0 && grid > static_cast<unsigned>(AR_SUM_GRID_CAP))
+        grid = AR_SUM_GRID_CAP;
+    if (log_enabled())
+        fprintf(stderr, "[ar] sum pack R=%d V=%d n=%zu grid=%u block=%d unroll=%d\n", R, E::V, a.n, grid, T, U);
+    hipLaunchKernelGGL((ar_sum_pack_kernel<E, R, T, U>), dim3(grid), dim3(T), 0, stream, a);
+}
+
+int current_device();
+int device_cus(int dev);
+
 template <class E, int R>
 int32_t launch_sum(const ar_params_t *p, hipStream_t stream, bool vec)
 {
@@ -714,14 +780,11 @@ int32_t launch_sum(const ar_params_t *p, hipStream_t stream, bool vec)
     a.n = p->elts_total;
     if (vec) {
         a.npacks = a.n / E::V;
-        constexpr int T = SumShape<R>::kThreads, U = SumShape<R>::kUnroll;
-        const size_t step = static_cast<size_t>(T) * U;
-        unsigned grid = clamp_grid(a.npacks / step);
-        if (AR_SUM_GRID_CAP > 0 && grid > static_cast<unsigned>(AR_SUM_GRID_CAP))
-            grid = AR_SUM_GRID_CAP;
-        if (log_enabled())
-            fprintf(stderr, "[ar] sum pack R=%d V=%d n=%zu grid=%u block=%d unroll=%d\n", R, E::V, a.n, grid, T, U);
-        hipLaunchKernelGGL((ar_sum_pack_kernel<E, R, T, U>), dim3(grid), dim3(T), 0, stream, a);
+        const size_t cus = static_cast<size_t>(device_cus(current_device()));
+        if (a.npacks < cus * kSumSmallPacksPerCU)
+            launch_sum_as<E, R, kSumSmallThreads, kSumSmallUnroll>(a, stream);
+        else
+            launch_sum_as<E, R, SumShape<R>::kThreads, SumShape<R>::kUnroll>(a, stream);
     } else {
         const unsigned grid = clamp_grid((a.n + kElemThreads - 1) / kElemThreads);
         if (log_enabled())

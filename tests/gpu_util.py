@@ -29,21 +29,14 @@ def dev(a: np.ndarray, dtype: str) -> torch.Tensor:
 
 
 def slab(host_parts, dtype: str):
-    """Device copies of the partials placed in one allocation at the slot
-    offsets of ar_partials_layout; returns (allocation, views)."""
+    """Device copies of the partials placed in one allocation from
+    ar.allocate_workspace (the slots of ar_partials_layout); returns
+    (allocation, views)."""
     from tensor_all_reduce_ar_amd import ar
-    code = {"fp32": ar.AR_FP32, "fp16": ar.AR_FP16, "bf16": ar.AR_BF16}[dtype]
-    n = host_parts[0].size
-    st, offs, total = ar.ar_partials_layout(n, code, len(host_parts))
-    assert st == ar.AR_OK
-    base = torch.empty(total, dtype=torch.uint8, device="cuda")
-    size = 4 if dtype == "fp32" else 2
-    views = []
-    for off, h in zip(offs, host_parts):
-        v = base[off:off + n * size].view(TORCH_DT[dtype])
+    ws = ar.allocate_workspace(host_parts[0].size, TORCH_DT[dtype], len(host_parts))
+    for v, h in zip(ws.partials, host_parts):
         v.copy_(dev(h, dtype))
-        views.append(v)
-    return base, views
+    return ws.buffer, ws.partials
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:

@@ -401,3 +401,15 @@ def test_rmsnorm_entry_needs_one_input():
     assert ar.call("ar_rmsnorm", fused_params(ranks=2)) == ar.AR_ERR_RANKS
     assert ar.call("ar_rmsnorm", fused_params(ranks=1, hidden=0)) == ar.AR_ERR_SHAPE
     assert ar.load().ar_rmsnorm(None, None) == ar.AR_ERR_NULL
+
+
+def test_allocate_workspace_rejects_what_the_layout_rejects():
+    """The allocator asks ar_partials_layout first, so a bad rank count or a
+    size that does not fit fails before any device allocation."""
+    import torch
+    with pytest.raises(ar.ArError, match="AR_ERR_RANKS"):
+        ar.allocate_workspace(100, torch.float16, 9)
+    with pytest.raises(ar.ArError, match="AR_ERR_SHAPE"):
+        ar.allocate_workspace((1 << 62) + 1, torch.float32, 8)
+    with pytest.raises(TypeError):
+        ar.allocate_workspace(100, torch.int32, 2)

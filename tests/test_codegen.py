@@ -98,3 +98,16 @@ def test_ceiling_store_forms(libceiling):
     sc1 = re.findall(r"buffer_store_dwordx4 .*", asm)
     assert sc1, "16-byte buffer stores"
     assert all(re.search(r"\bsc1\b", x) and not re.search(r"\b(nt|sc0)\b", x) for x in sc1), sc1[:3]
+
+
+def test_row_sums_reduce_through_dpp_not_lds_permutes(libar):
+    """The wave-level sum of squares moves lanes with DPP (pair and quad
+    swaps, row mirrors, the row broadcasts 15 and 31) and reads the total back
+    with v_readlane; no ds_bpermute (an LDS round trip per step) is left."""
+    asm, _ = libar
+    ops = _mnemonics(asm)
+    assert "ds_bpermute_b32" not in ops
+    for ctrl in (r"quad_perm:\[1,0,3,2\]", r"quad_perm:\[2,3,0,1\]", r"row_half_mirror", r"row_mirror",
+                 r"row_bcast:15 row_mask:0xa", r"row_bcast:31 row_mask:0xc"):
+        assert re.search(r"_dpp .*" + ctrl, asm), ctrl
+    assert "v_readlane_b32" in ops

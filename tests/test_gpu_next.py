@@ -199,3 +199,39 @@ def test_large_fused_workload_in_the_recommended_layout():
     assert_bitexact(host_bits(inter), ref_inter, w.dtype, "large fused, slab layout, intermediate")
     assert_output_close(host_bits(out), ref_out, w.dtype, "large fused, slab layout, output")
     del base
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allocate_workspace_places_partials_at_the_layout_slots(dtype):
+    """ar.allocate_workspace (the one-GPU counterpart of "allreduce.d2"
+    CustomAllReduceHelper.allocate_workspace): one allocation, R typed views at
+    exactly the byte offsets ar_partials_layout reports, 256-byte aligned and
+    disjoint; writing the partials into the views and running both ops on them
+    gives the oracle's results."""
+    ranks, rows, hidden = 4, 33, 2560
+    note(f"[next] allocate_workspace {dtype} R={ranks}")
+    w = inputs.random_fused(dtype, ranks, rows, hidden, 1700)
+    code = {"fp32": ar.AR_FP32, "fp16": ar.AR_FP16, "bf16": ar.AR_BF16}[dtype]
+    st, offs, total = ar.ar_partials_layout(w.n, code, ranks)
+    ws = ar.allocate_workspace(w.n, {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[dtype],
+                               ranks)
+    assert st == ar.AR_OK and ws.offsets == offs and ws.total_bytes == total == ws.buffer.numel()
+    base = ws.buffer.data_ptr()
+    for r, v in enumerate(ws.partials):
+        assert v.is_contiguous() and v.numel() == w.n and v.data_ptr() - base == offs[r]
+        assert v.data_ptr() % 256 == 0
+        v.copy_(dev(w.partials[r], dtype))
+    out, inter, s_out = Guarded(w.n, dtype), Guarded(w.n, dtype), Guarded(w.n, dtype)
+    ar.ar_residual_rmsnorm(ws.partials, dev(w.weight, dtype), w.eps, out.t, inter.t, bias=dev(w.bias, dtype),
+                           residual=dev(w.residual, dtype))
+    ar.ar_sum(ws.partials, s_out.t)
+    torch.cuda.synchronize()
+    for g in (out, inter, s_out):
+        g.check_guards()
+    ref_out, ref_inter = oracle_fused(w)
+    assert_bitexact(host_bits(inter.t), ref_inter, dtype, "workspace intermediate")
+    assert_output_close(host_bits(out.t), ref_out, dtype, "workspace output")
+    assert_bitexact(host_bits(s_out.t), bits(oracle_sum(w)), dtype, "workspace sum")
+    # the slots were not disturbed by the calls (inputs are read only)
+    for r, v in enumerate(ws.partials):
+        assert_bitexact(host_bits(v), bits(w.partials[r]), dtype, f"workspace slot {r} after the calls")
