@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "effective HBM GB/s and % of peak, fused AR+residual+RMSNorm, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
 LLC_BYTES = 256 << 20   # MI355X Infinity Cache
+MIN_TIMED_CALLS = 20    # every timed configuration is timed over at least this many calls
 FUSED_KERNEL = "ar_rmsnorm_pack_kernel"
 SUM_KERNEL = "ar_sum_pack_kernel"
 
@@ -51,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the unfused and two-shot line items")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (repeats the sample)")
+    ap.add_argument("--min-calls", type=int, default=MIN_TIMED_CALLS,
+                    help="calls timed for every workload but the headline (which takes --steps)")
     return ap.parse_args()
 
 
@@ -85,8 +88,9 @@ def rotation_sets(bytes_per_set: int, out_bytes_per_set: int) -> int:
 
 
 def time_launches(torch, launch, nsets, steps, warmup, stream):
-    """Whole-region timing (ms per step) and per-launch kernel timing (ms),
-    both with HIP events on the launch stream."""
+    """Whole-region timing (ms per step over `steps` back-to-back launches) and
+    per-launch timing (a list of `steps` kernel durations in ms, each between
+    two events around one launch), both with HIP events on the launch stream."""
     for i in range(warmup):
         launch(i % nsets)
     torch.cuda.synchronize()
@@ -97,15 +101,28 @@ def time_launches(torch, launch, nsets, steps, warmup, stream):
     stop.record(stream)
     torch.cuda.synchronize()
     region_ms = start.elapsed_time(stop)
-    # per-launch events: the average duration of one kernel launch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(evs):
         a.record(stream)
         launch(i % nsets)
         b.record(stream)
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in evs]
-    return region_ms / steps, statistics.mean(per), statistics.median(per), min(per)
+    return region_ms / steps, [a.elapsed_time(b) for a, b in evs]
+
+
+OUTLIER_FACTOR = 1.5
+
+
+def launch_stats(per_ms):
+    """Median / min / max / mean of per-launch durations (us), and the
+    launches slower than OUTLIER_FACTOR x the median, flagged by index."""
+    us = [x * 1e3 for x in per_ms]
+    med = statistics.median(us)
+    out = [(i, round(x, 2)) for i, x in enumerate(us) if x > OUTLIER_FACTOR * med]
+    return {"launches": len(us), "median": round(med, 2), "min": round(min(us), 2), "max": round(max(us), 2),
+            "mean": round(statistics.mean(us), 2), "mean_without_outliers":
+                round(statistics.mean([x for x in us if x <= OUTLIER_FACTOR * med]), 2),
+            "outliers": {"rule": f"> {OUTLIER_FACTOR} x median", "count": len(out), "index_us": out}}
 
 
 def dev(torch, a, dtype):
@@ -117,19 +134,13 @@ def dev(torch, a, dtype):
 
 
 def slab_copies(torch, ar, parts):
-    """Copies of the device partials in one allocation at the slot offsets of
-    ar_partials_layout; returns (allocation, views)."""
-    code = {torch.float32: ar.AR_FP32, torch.float16: ar.AR_FP16, torch.bfloat16: ar.AR_BF16}[parts[0].dtype]
-    n, size = parts[0].numel(), parts[0].element_size()
-    st, offs, total = ar.ar_partials_layout(n, code, len(parts))
-    assert st == ar.AR_OK, ar.ar_status_string(st)
-    base = torch.empty(total, dtype=torch.uint8, device="cuda")
-    views = []
-    for off, p in zip(offs, parts):
-        v = base[off:off + n * size].view(p.dtype)
+    """Copies of the device partials in one allocation from
+    ar.allocate_workspace (the slots of ar_partials_layout); returns
+    (allocation, views)."""
+    ws = ar.allocate_workspace(parts[0].numel(), parts[0].dtype, len(parts))
+    for v, p in zip(ws.partials, parts):
         v.copy_(p)
-        views.append(v)
-    return base, views
+    return ws.buffer, ws.partials
 
 
 def bench_fused(torch, ar, w, args, stream, layout="separate"):
@@ -157,7 +168,7 @@ def bench_fused(torch, ar, w, args, stream, layout="separate"):
         parts, res, out, inter = sets[k]
         ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res, stream=stream)
 
-    ms_step, k_mean, k_med, k_min = time_launches(torch, launch, nsets, args.steps, args.warmup, stream)
+    ms_step, per = time_launches(torch, launch, nsets, args.steps, args.warmup, stream)
     out_bits, inter_bits = host_bits(torch, sets[0][2]), host_bits(torch, sets[0][3])
 
     # The practical ceiling on the same buffers: every partial and the
@@ -168,29 +179,37 @@ def bench_fused(torch, ar, w, args, stream, layout="separate"):
 
     ceil_bytes = (w.ranks + (w.residual is not None) + 2) * w.n * w.itemsize
     ceil = stream_ceiling_on(torch, streams, nsets, ceil_bytes, args.steps, args.warmup, stream)
-    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, k_mean=k_mean, k_med=k_med, k_min=k_min,
+    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, per=launch_stats(per), steps=args.steps,
                 out_bits=out_bits, inter_bits=inter_bits, ceil=ceil)
 
 
-def bench_sum(torch, ar, w, args, stream):
+def bench_sum(torch, ar, w, args, stream, layout="separate"):
+    """layout as for bench_fused."""
     nb = w.algorithmic_bytes()
     nsets = rotation_sets(nb, w.n * w.itemsize)
     base = [dev(torch, p, w.dtype) for p in w.partials]
-    sets = []
+    sets, keep = [], []
     for k in range(nsets):
-        parts = base if k == 0 else [p.clone() for p in base]
+        if layout == "slab":
+            slab, parts = slab_copies(torch, ar, base)
+            keep.append(slab)
+        else:
+            parts = base if k == 0 else [p.clone() for p in base]
         sets.append((parts, torch.empty_like(base[0])))
+    if layout == "slab":
+        del base
 
     def launch(k):
         ar.ar_sum(sets[k][0], sets[k][1], stream=stream)
 
-    steps = max(5, args.steps // 2)
-    ms_step, k_mean, k_med, k_min = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
+    steps = max(args.min_calls, args.steps)
+    ms_step, per = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
+    out_bits = host_bits(torch, sets[0][1])
 
     # the same buffers, read and written once, nothing else
     ceil = stream_ceiling_on(torch, lambda k: (sets[k][0], [sets[k][1]]), nsets, nb, steps,
                              max(2, args.warmup // 2), stream)
-    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, k_mean=k_mean, k_med=k_med, k_min=k_min, steps=steps,
+    return dict(bytes=nb, nsets=nsets, ms_step=ms_step, per=launch_stats(per), steps=steps, out_bits=out_bits,
                 ceil=ceil)
 
 
@@ -217,8 +236,8 @@ def bench_unfused(torch, ar, w, args, stream):
         ar.ar_sum(parts, x, stream=stream)
         ar.ar_rmsnorm(x, weight, w.eps, out, inter, bias=bias, residual=res, stream=stream)
 
-    steps = max(5, args.steps // 2)
-    ms_step, *_ = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
+    steps = max(args.min_calls, args.steps)
+    ms_step, _ = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
     return dict(bytes=nb, nsets=nsets, ms_step=ms_step, steps=steps)
 
 
@@ -257,8 +276,8 @@ def bench_slice(torch, ar, w, args, stream, num):
         else:
             ar.ar_residual_rmsnorm_slice(parts, weight, w.eps, out, inter, 0, num, residual=res, stream=st)
 
-    steps = max(5, args.steps // 2)
-    ms_step, *_ = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
+    steps = max(args.min_calls, args.steps)
+    ms_step, _ = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
 
     # The same calls replayed from a HIP graph (one call per rotating set),
     # which takes the host's launch cost out of a call this small.
@@ -285,57 +304,57 @@ def bench_slice(torch, ar, w, args, stream, num):
     return dict(bytes=nb, elements=m, nsets=nsets, ms_step=ms_step, steps=steps, graph_ms=graph_ms)
 
 
-def small_op_latency(torch, ar, inputs, stream, calls=20, reps=10):
-    """Per-call time of the launch-bound workloads, eager (back-to-back
-    launches) and replayed from a HIP graph of `calls` back-to-back calls,
-    which takes the host's launch cost out."""
-    names = [inputs.SUM_FP32_R2_4x256, inputs.FUSED_FP16_R8_16x4096, inputs.SUM_FP16_R2_1000003] + \
-        [inputs.fused_fp16_r2_5120_name(t) for t in (1, 7, 64)]
-    outl = {}
-    for name in names:
-        w = inputs.make(name)
-        parts = [dev(torch, p, w.dtype) for p in w.partials]
-        out = torch.empty_like(parts[0])
-        if w.op == "sum":
-            def call():
-                ar.ar_sum(parts, out)
-        else:
-            inter = torch.empty_like(parts[0])
-            weight, res = dev(torch, w.weight, w.dtype), dev(torch, w.residual, w.dtype)
-            bias = dev(torch, w.bias, w.dtype) if w.bias is not None else None
+def bench_small(torch, ar, w, stream, calls=20, reps=20):
+    """A launch-bound workload on one set of buffers (warm in cache, as right
+    after the GEMMs that produce the partials): per-call time of eager
+    back-to-back launches through the binding, and of a HIP graph of `calls`
+    back-to-back calls replayed `reps` times (one per-call figure per replay),
+    which takes the host's launch cost out. Returns the outputs of the last
+    call as raw bits."""
+    parts = [dev(torch, p, w.dtype) for p in w.partials]
+    out = torch.empty_like(parts[0])
+    inter = None
+    if w.op == "sum":
+        def call(st=None):
+            ar.ar_sum(parts, out, stream=st)
+    else:
+        inter = torch.empty_like(parts[0])
+        weight, res = dev(torch, w.weight, w.dtype), dev(torch, w.residual, w.dtype)
+        bias = dev(torch, w.bias, w.dtype) if w.bias is not None else None
 
-            def call():
-                ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res)
-        for _ in range(3):
-            call()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(calls * reps):
-            call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        eager = a.elapsed_time(b) * 1e3 / (calls * reps)
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for _ in range(calls):
-                    call()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
+        def call(st=None):
+            ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res, stream=st)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(calls * reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    eager = a.elapsed_time(b) * 1e3 / (calls * reps)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(calls):
+                call(side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for x, y in evs:
+        x.record(stream)
         g.replay()
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
-            g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        graph = a.elapsed_time(b) * 1e3 / (calls * reps)
-        outl[name] = {"bytes": w.algorithmic_bytes(), "eager_us": round(eager, 2), "graph_us": round(graph, 2)}
-        del g
-    return outl
+        y.record(stream)
+    torch.cuda.synchronize()
+    per_call = [x.elapsed_time(y) / calls for x, y in evs]  # ms
+    del g
+    return dict(eager_us=eager, per_call=per_call, calls=calls, reps=reps, out_bits=host_bits(torch, out),
+                inter_bits=host_bits(torch, inter) if inter is not None else None)
 
 
 def stream_ceiling_on(torch, streams, nsets, nbytes, steps, warmup, stream):
@@ -348,7 +367,7 @@ def stream_ceiling_on(torch, streams, nsets, nbytes, steps, warmup, stream):
         def launch(k, shape=shape):
             ins, outs = streams(k)
             sc.sc_stream(ins, outs, shape, stream=stream)
-        ms, *_ = time_launches(torch, launch, nsets, steps, warmup, stream)
+        ms, _ = time_launches(torch, launch, nsets, steps, warmup, stream)
         per[label] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     best = max(per, key=per.get)
     return {"gbps": per[best], "shape": best, "per_shape_gbps": per}
@@ -387,61 +406,94 @@ def stream_ceilings(torch, stream):
     return {k: round(v, 1) for k, v in out.items()}
 
 
-def cpu_baseline(w, seconds):
-    """The CPU oracle (single-threaded C) on the same inputs, repeated over the
-    whole workload until `seconds` have passed (at least once)."""
+def oracle_call(w, lo=0, hi=None, out=None, inter=None):
+    """The CPU oracle on rows [lo, hi) of a fused workload, or on elements
+    [lo, hi) of a sum, writing into `out` (and `inter`) at the same places."""
     import numpy as np
 
     import oracle
-    out = np.zeros(w.n, dtype=w.partials[0].dtype)
-    inter = np.zeros(w.n, dtype=w.partials[0].dtype)
-    times = []
-    t_end = time.perf_counter() + seconds
-    while True:
-        t0 = time.perf_counter()
-        oracle.ar_residual_rmsnorm(w.dtype, w.partials, w.hidden, w.weight, w.eps, out, inter, bias=w.bias,
-                                   residual=w.residual)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() >= t_end or len(times) >= 20:
-            break
-    t = statistics.median(times)
-    return t, len(times), out, inter
+    if w.op == "sum":
+        hi = w.n if hi is None else hi
+        oracle.ar_sum(w.dtype, [p[lo:hi] for p in w.partials], out[lo:hi])
+        return
+    hi = w.rows if hi is None else hi
+    H = w.hidden
+    sl = slice(lo * H, hi * H)
+    oracle.ar_residual_rmsnorm(w.dtype, [p[sl] for p in w.partials], H, w.weight, w.eps, out[sl], inter[sl],
+                               bias=w.bias, residual=w.residual[sl] if w.residual is not None else None)
 
 
-def cpu_oracle_all_cores(w, seconds):
-    """The same single-threaded oracle on every host core at once, each thread
-    over a contiguous block of rows (rows are independent, and the ctypes call
-    releases the GIL). Returns (median s per call, repeats, threads, out, inter)."""
+def host_threads() -> int:
+    """Host threads the all-core oracle uses: the CPUs this process may run
+    on (at most 16, the GPU host's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def oracle_timed(w, runs_1t, runs_nt, seconds):
+    """The oracle as it stands, on 1 thread and on every host core at once
+    (contiguous blocks of rows, or of elements for the sum; the ctypes call
+    releases the GIL). Each leg repeats until `runs` runs or `seconds` have
+    passed, at least once. Returns the 1-thread result arrays, both medians
+    (s), run counts, threads, and whether the all-core result is bitwise the
+    1-thread one."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
+    dt = w.partials[0].dtype
+    out, inter = np.zeros(w.n, dt), (np.zeros(w.n, dt) if w.op == "fused" else None)
 
-    import oracle
-    try:
-        threads = len(os.sched_getaffinity(0))
-    except AttributeError:
-        threads = os.cpu_count() or 1
-    threads = max(1, min(threads, 16, w.rows))
-    H = w.hidden
-    out = np.zeros(w.n, dtype=w.partials[0].dtype)
-    inter = np.zeros_like(out)
-    blocks = [(w.rows * k // threads, w.rows * (k + 1) // threads) for k in range(threads)]
-
-    def block(b):
-        sl = slice(b[0] * H, b[1] * H)
-        oracle.ar_residual_rmsnorm(w.dtype, [p[sl] for p in w.partials], H, w.weight, w.eps, out[sl], inter[sl],
-                                   bias=w.bias, residual=w.residual[sl] if w.residual is not None else None)
-
-    times = []
-    t_end = time.perf_counter() + seconds
-    with ThreadPoolExecutor(threads) as ex:
+    def repeat(fn, runs):
+        times, t_end = [], time.perf_counter() + seconds
         while True:
             t0 = time.perf_counter()
-            list(ex.map(block, blocks))
+            fn()
             times.append(time.perf_counter() - t0)
-            if time.perf_counter() >= t_end or len(times) >= 20:
-                break
-    return statistics.median(times), len(times), threads, out, inter
+            if len(times) >= runs or time.perf_counter() >= t_end:
+                return statistics.median(times), len(times)
+
+    t1, n1 = repeat(lambda: oracle_call(w, out=out, inter=inter), runs_1t)
+    units = w.n if w.op == "sum" else w.rows
+    threads = max(1, min(host_threads(), units))
+    blocks = [(units * k // threads, units * (k + 1) // threads) for k in range(threads)]
+    m_out, m_inter = np.zeros_like(out), (np.zeros_like(inter) if inter is not None else None)
+    with ThreadPoolExecutor(threads) as ex:
+        tn, nn = repeat(lambda: list(ex.map(lambda b: oracle_call(w, b[0], b[1], m_out, m_inter), blocks)), runs_nt)
+    same = bool(np.array_equal(m_out, out) and (inter is None or np.array_equal(m_inter, inter)))
+    return dict(out=out, inter=inter, t1=t1, n1=n1, tn=tn, nn=nn, threads=threads, nt_bitexact=same)
+
+
+def compare_to_oracle(w, gpu_out, gpu_inter, ref_out, ref_inter):
+    """The comparison rules: sums and pre-norm sums bitwise (NaN == NaN);
+    normed outputs within 2 ulp (fp16/bf16: the distance between
+    order-preserving integer encodings, +0 == -0) or 1e-5 relative (fp32)."""
+    import numpy as np
+
+    def bits(a):
+        return a.view(np.uint32 if a.dtype.itemsize == 4 else np.uint16)
+
+    def ordered(b):
+        b = b.astype(np.int64)
+        sign = 0x80000000 if w.dtype == "fp32" else 0x8000
+        return np.where(b & sign, sign - b, b)
+
+    rec = {}
+    if w.op == "sum":
+        rec["bitexact"] = bool(np.array_equal(gpu_out, bits(ref_out)))
+        rec["max_ulp"] = int(np.abs(ordered(gpu_out) - ordered(bits(ref_out))).max())
+        return rec
+    rec["intermediate_bitexact"] = bool(np.array_equal(gpu_inter, bits(ref_inter)))
+    rec["output_max_ulp"] = int(np.abs(ordered(gpu_out) - ordered(bits(ref_out))).max())
+    if w.dtype == "fp32":
+        g, r = gpu_out.view(np.float32).astype(np.float64), ref_out.astype(np.float64)
+        rec["output_max_rel"] = float(np.max(np.abs(g - r) / np.maximum(np.abs(r), 1e-300)))
+        rec["within_tolerance"] = bool(rec["intermediate_bitexact"] and rec["output_max_rel"] <= 1e-5)
+    else:
+        rec["within_tolerance"] = bool(rec["intermediate_bitexact"] and rec["output_max_ulp"] <= 2)
+    return rec
 
 
 def host_cpu_model() -> str:
@@ -461,6 +513,24 @@ def host_bits(torch, t):
     if t.element_size() == 4:
         return t.view(torch.int32).numpy().view(np.uint32)
     return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def workload_record(w, nbytes, timing, stats, extra=None):
+    """One workload's GPU figures: per-call median / min / max (us), GB/s and
+    fraction of the HBM peak at the median, and how they were timed."""
+    rec = {"op": "sum" if w.op == "sum" else "fused", "ranks": w.ranks, "dtype": w.dtype,
+           "shape": [w.n] if w.op == "sum" else [w.rows, w.hidden], "bias": w.bias is not None,
+           "seeds": w.seeds, "bytes": nbytes, "timing": timing,
+           "gpu_us_median": stats["median"], "gpu_us_min": stats["min"], "gpu_us_max": stats["max"],
+           "gbps_at_median": round(nbytes / (stats["median"] * 1e-6) / 1e9, 1),
+           "pct_of_peak_at_median": round(100 * nbytes / (stats["median"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+           "per_call_us": stats}
+    rec.update(extra or {})
+    return rec
+
+
+COLD = "cold: rotating input sets (whole cycle >= 4x the 256 MB cache), HIP events around each launch"
+WARM = "warm: one set of buffers, a HIP graph of 20 back-to-back calls replayed 20 times (one figure per replay)"
 
 
 def main():
@@ -492,10 +562,13 @@ def main():
     # One launch per step, back to back on one stream (no gaps between them):
     # the region time per step is the average launch duration.
     achieved = gbps
-    print(f"[bench] fused: {f['ms_step'] * 1e3:.1f} us/step ({achieved:.0f} GB/s); isolated launches "
-          f"{f['k_mean'] * 1e3:.1f} us; streaming ceiling on the same buffers {f['ceil']['gbps']:.0f} GB/s",
+    print(f"[bench] fused: {f['ms_step'] * 1e3:.1f} us/step ({achieved:.0f} GB/s); isolated launches median "
+          f"{f['per']['median']:.1f} us; streaming ceiling on the same buffers {f['ceil']['gbps']:.0f} GB/s",
           file=sys.stderr, flush=True)
-    gpu_out, gpu_inter = f.pop("out_bits"), f.pop("inter_bits")
+    gpu = {name: (w, f.pop("out_bits"), f.pop("inter_bits"))}  # outputs to check against the oracle
+    records = {name: workload_record(w, f["bytes"], COLD, f["per"], {
+        "us_per_call_back_to_back": round(f["ms_step"] * 1e3, 2), "rotating_input_sets": f["nsets"],
+        "stream_ceiling_same_buffers_gbps": f["ceil"]["gbps"]})}
 
     result = {
         "metric": METRIC,
@@ -524,8 +597,7 @@ def main():
             "stream_ceiling_same_buffers": f["ceil"],
             "frac_of_stream_ceiling": round(achieved / f["ceil"]["gbps"], 4),
             "launch_us": round(f["ms_step"] * 1e3, 2), "algorithmic_bytes_per_launch": f["bytes"],
-            "isolated_launch_us": {"mean": round(f["k_mean"] * 1e3, 2), "median": round(f["k_med"] * 1e3, 2),
-                                   "min": round(f["k_min"] * 1e3, 2)},
+            "isolated_launch_us": f["per"],
         },
     }
 
@@ -535,21 +607,35 @@ def main():
         s_ach = s["bytes"] / (s["ms_step"] * 1e-3) / 1e9
         result["standalone_sum"] = {
             "workload": sw.name, "kernel": SUM_KERNEL, "bytes_per_call": s["bytes"],
-            "us_per_call": round(s["ms_step"] * 1e3, 2), "isolated_launch_us_mean": round(s["k_mean"] * 1e3, 2),
-            "gbps": round(s["bytes"] / (s["ms_step"] * 1e-3) / 1e9, 1), "achieved": round(s_ach, 1),
+            "us_per_call": round(s["ms_step"] * 1e3, 2), "isolated_launch_us": s["per"],
+            "gbps": round(s_ach, 1), "achieved": round(s_ach, 1),
             "frac": round(s_ach / HBM_PEAK_GBPS, 4), "steps": s["steps"], "rotating_input_sets": s["nsets"],
             "traffic": measured_traffic(SUM_KERNEL, sw.name),
             "stream_ceiling_same_buffers": s["ceil"],
             "frac_of_stream_ceiling": round(s_ach / s["ceil"]["gbps"], 4),
         }
+        gpu[sw.name] = (sw, s.pop("out_bits"), None)
+        if not args.no_next:
+            sl = bench_sum(torch, ar, sw, args, stream, layout="slab")
+            sl_gbps = sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9
+            result["standalone_sum"]["partials_in_layout"] = {
+                "what": "the same sum with each set's partials in one allocation from allocate_workspace",
+                "us_per_call": round(sl["ms_step"] * 1e3, 2), "gbps": round(sl_gbps, 1),
+                "frac": round(sl_gbps / HBM_PEAK_GBPS, 4), "stream_ceiling_same_buffers": sl["ceil"],
+                "frac_of_stream_ceiling": round(sl_gbps / sl["ceil"]["gbps"], 4),
+                "gpu_matches_separate_layout": bool(np.array_equal(sl["out_bits"], gpu[sw.name][1])),
+            }
+            del sl
+        records[sw.name] = workload_record(sw, s["bytes"], COLD, s["per"], {
+            "us_per_call_back_to_back": round(s["ms_step"] * 1e3, 2), "rotating_input_sets": s["nsets"],
+            "stream_ceiling_same_buffers_gbps": s["ceil"]["gbps"]})
         print(f"[bench] sum: {s['ms_step'] * 1e3:.1f} us/call ({s_ach:.0f} GB/s)", file=sys.stderr, flush=True)
-        del sw
 
     if not args.no_next:
         u = bench_unfused(torch, ar, w, args, stream)
         result["unfused_baseline"] = {
             "what": "ar_sum into a buffer, then ar_rmsnorm on it (two launches)",
-            "us_per_call": round(u["ms_step"] * 1e3, 2), "bytes_per_call": u["bytes"],
+            "us_per_call": round(u["ms_step"] * 1e3, 2), "bytes_per_call": u["bytes"], "steps": u["steps"],
             "gbps": round(u["bytes"] / (u["ms_step"] * 1e-3) / 1e9, 1),
             "fused_us_per_call": round(f["ms_step"] * 1e3, 2),
             "time_saved_by_fusion": round(1 - f["ms_step"] / u["ms_step"], 4),
@@ -559,21 +645,21 @@ def main():
         result["two_shot_share"] = {
             "what": f"slice 0 of {w.ranks} of the fused op (one rank's share of a two-shot split)",
             "elements": sl["elements"], "bytes_per_call": sl["bytes"], "us_per_call": round(sl["ms_step"] * 1e3, 2),
-            "gbps": round(sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9, 1),
+            "gbps": round(sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9, 1), "steps": sl["steps"],
             "graph_us_per_call": round(sl["graph_ms"] * 1e3, 2),
             "graph_gbps": round(sl["bytes"] / (sl["graph_ms"] * 1e-3) / 1e9, 1),
         }
         print(f"[bench] two-shot share: {sl['ms_step'] * 1e3:.1f} us/call eager, {sl['graph_ms'] * 1e3:.1f} us/call "
               f"from a HIP graph", file=sys.stderr, flush=True)
 
-    if not args.no_next:
+        gpu_out, gpu_inter = gpu[name][1], gpu[name][2]
         sl = bench_fused(torch, ar, w, args, stream, layout="slab")
         sl_gbps = sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9
         result["fused_partials_in_layout"] = {
-            "what": "the same fused workload with each set's partials in one allocation at the slots of "
-                    "ar_partials_layout (4 KiB more stagger per partial)",
+            "what": "the same fused workload with each set's partials in one allocation from allocate_workspace "
+                    "(the slots of ar_partials_layout: 4 KiB more stagger per partial)",
             "us_per_call": round(sl["ms_step"] * 1e3, 2), "gbps": round(sl_gbps, 1),
-            "frac": round(sl_gbps / HBM_PEAK_GBPS, 4),
+            "frac": round(sl_gbps / HBM_PEAK_GBPS, 4), "isolated_launch_us": sl["per"],
             "stream_ceiling_same_buffers": sl["ceil"],
             "frac_of_stream_ceiling": round(sl_gbps / sl["ceil"]["gbps"], 4),
             "gpu_matches_separate_layout": bool(np.array_equal(sl["out_bits"], gpu_out) and
@@ -589,40 +675,65 @@ def main():
             "workload": mw.name, "kernel": FUSED_KERNEL, "bytes_per_call": m["bytes"],
             "us_per_call": round(m["ms_step"] * 1e3, 2), "gbps": round(m_gbps, 1),
             "frac": round(m_gbps / HBM_PEAK_GBPS, 4), "rotating_input_sets": m["nsets"],
-            "traffic": measured_traffic(FUSED_KERNEL, mw.name),
+            "isolated_launch_us": m["per"], "traffic": measured_traffic(FUSED_KERNEL, mw.name),
             "stream_ceiling_same_buffers": m["ceil"],
             "frac_of_stream_ceiling": round(m_gbps / m["ceil"]["gbps"], 4),
         }
+        gpu[mw.name] = (mw, m.pop("out_bits"), m.pop("inter_bits"))
+        records[mw.name] = workload_record(mw, m["bytes"], COLD, m["per"], {
+            "us_per_call_back_to_back": round(m["ms_step"] * 1e3, 2), "rotating_input_sets": m["nsets"],
+            "stream_ceiling_same_buffers_gbps": m["ceil"]["gbps"]})
         print(f"[bench] fused fp16 R=2 4096x5120: {m['ms_step'] * 1e3:.1f} us/call ({m_gbps:.0f} GB/s)",
               file=sys.stderr, flush=True)
-        del mw, m
-        result["small_op_latency"] = small_op_latency(torch, ar, inputs, stream)
-        print("[bench] small-op latency done", file=sys.stderr, flush=True)
+
+        small = [inputs.SUM_FP32_R2_4x256, inputs.FUSED_FP16_R8_16x4096, inputs.SUM_FP16_R2_1000003] + \
+            [inputs.fused_fp16_r2_5120_name(t) for t in (1, 7, 64)]
+        for nm in small:
+            sw_ = inputs.make(nm)
+            r = bench_small(torch, ar, sw_, stream)
+            stats = launch_stats(r["per_call"])
+            stats["launches"] = r["calls"] * r["reps"]
+            records[nm] = workload_record(sw_, sw_.algorithmic_bytes(), WARM, stats, {
+                "eager_us_per_call": round(r["eager_us"], 2), "graph_replays": r["reps"]})
+            gpu[nm] = (sw_, r["out_bits"], r["inter_bits"])
+        print("[bench] launch-bound workloads done", file=sys.stderr, flush=True)
 
     ceilings = stream_ceilings(torch, stream)
     result["copy_ceiling_gbps"] = ceilings["copy_gbps"]
     result["stream_ceilings_1gib"] = ceilings
 
     if not args.no_cpu_baseline:
-        t, reps, ref_out, ref_inter = cpu_baseline(w, args.cpu_seconds)
-        sig_ok = np.array_equal(gpu_inter, ref_inter.view(gpu_inter.dtype))
-        o = lambda b: np.where(b.astype(np.int64) & 0x8000, 0x8000 - b.astype(np.int64), b.astype(np.int64))
-        ulp = int(np.abs(o(gpu_out) - o(ref_out.view(np.uint16))).max()) if w.dtype != "fp32" else None
-        tm, mreps, threads, m_out, m_inter = cpu_oracle_all_cores(w, args.cpu_seconds / 2)
-        result["cpu_baseline"] = {
-            "value": round(w.algorithmic_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole {name} call ({w.rows} rows), {reps} run(s), median {t:.2f} s",
-            "host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count(),
-            "gpu_vs_oracle": {"intermediate_bitexact": bool(sig_ok), "output_max_ulp": ulp},
-            "all_cores": {
-                "value": round(w.algorithmic_bytes() / tm / 1e9, 4), "unit": "GB/s", "cores": threads,
-                "sample": f"the same call split into {threads} row blocks, one thread each, {mreps} run(s), "
-                          f"median {tm:.3f} s",
-                "bitexact_vs_one_thread": bool(np.array_equal(m_out, ref_out) and np.array_equal(m_inter, ref_inter)),
-            },
-        }
-        print(f"[bench] oracle: {t:.2f} s per call; {tm:.3f} s on {threads} threads", file=sys.stderr, flush=True)
-
+        # The oracle on the host, on the same inputs, checked against this run's
+        # GPU outputs: every workload on 1 thread and on every core; the
+        # headline workload's 1-thread rate is the reported CPU baseline.
+        for nm, (wk, g_out, g_inter) in gpu.items():
+            big = wk.algorithmic_bytes() > (64 << 20)
+            secs = args.cpu_seconds if nm == name else (8.0 if big else 2.0)
+            o = oracle_timed(wk, 3 if big else 20, 3 if big else 20, secs)
+            rec = records[nm]
+            rec["vs_oracle"] = compare_to_oracle(wk, g_out, g_inter, o["out"], o["inter"])
+            rec.update({"oracle_1t_ms": round(o["t1"] * 1e3, 3), "oracle_1t_runs": o["n1"],
+                        "oracle_nt_ms": round(o["tn"] * 1e3, 3), "oracle_nt_runs": o["nn"],
+                        "oracle_threads": o["threads"], "oracle_nt_bitexact_vs_1t": o["nt_bitexact"],
+                        "oracle_1t_gbps": round(wk.algorithmic_bytes() / o["t1"] / 1e9, 4),
+                        "oracle_nt_gbps": round(wk.algorithmic_bytes() / o["tn"] / 1e9, 4)})
+            if nm == name:
+                result["cpu_baseline"] = {
+                    "value": rec["oracle_1t_gbps"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+                    "sample": f"the whole {name} call ({wk.rows} rows), {o['n1']} run(s), median {o['t1']:.2f} s",
+                    "host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count(),
+                    "gpu_vs_oracle": rec["vs_oracle"],
+                    "all_cores": {
+                        "value": rec["oracle_nt_gbps"], "unit": "GB/s", "cores": o["threads"],
+                        "sample": f"the same call split into {o['threads']} row blocks, one thread each, "
+                                  f"{o['nn']} run(s), median {o['tn']:.3f} s",
+                        "bitexact_vs_one_thread": o["nt_bitexact"],
+                    },
+                }
+            print(f"[bench] oracle {nm}: {o['t1'] * 1e3:.1f} ms on 1 thread, {o['tn'] * 1e3:.1f} ms on "
+                  f"{o['threads']}; GPU vs oracle {rec['vs_oracle']}", file=sys.stderr, flush=True)
+    result["per_workload"] = records
+    result["host"] = {"cpu": host_cpu_model(), "logical_cpus": os.cpu_count(), "oracle_threads": host_threads()}
     result["versions"] = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
                           "source_hash": source_hash()}
     print(json.dumps(result), flush=True)

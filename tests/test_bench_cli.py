@@ -26,3 +26,50 @@ def test_multi_process_launch_is_refused():
     res = _run([], {"WORLD_SIZE": "4"})
     assert res.returncode == 2, res.stderr
     assert "--gpus 4 is not supported" in res.stderr
+
+
+# --------------------------------------------- the bench's host-side helpers
+sys.path.insert(0, ROOT)
+
+
+def test_launch_stats_flags_outliers():
+    import bench
+    per_ms = [0.0636] * 19 + [1.2]  # one launch 19x slower than the rest
+    st = bench.launch_stats(per_ms)
+    assert st["launches"] == 20 and st["median"] == 63.6 and st["min"] == 63.6 and st["max"] == 1200.0
+    assert st["outliers"]["count"] == 1 and st["outliers"]["index_us"] == [(19, 1200.0)]
+    assert st["mean"] > 100 and st["mean_without_outliers"] == 63.6
+
+
+def test_comparison_rules_of_the_bench():
+    """Bitwise for sums and pre-norm sums, ulp distance across zero for the
+    normed output (+0 and -0 are the same value)."""
+    import numpy as np
+
+    import bench
+    from tensor_all_reduce_ar_amd import inputs
+    w = inputs.random_fused("bf16", 2, 3, 16, 5)
+    ref = np.array([0x3F80, 0x8000, 0x0001] * 16, np.uint16)
+    got = ref.copy()
+    got[1] = 0x0000           # -0 vs +0: 0 ulp
+    got[2] = 0x8001           # smallest subnormals of either sign: 2 ulp apart
+    rec = bench.compare_to_oracle(w, got, ref.copy(), ref, ref)
+    assert rec == {"intermediate_bitexact": True, "output_max_ulp": 2, "within_tolerance": True}
+    got[0] = 0x3F83           # 3 ulp
+    assert not bench.compare_to_oracle(w, got, ref.copy(), ref, ref)["within_tolerance"]
+    s = inputs.random_sum("fp32", 2, 8, 5)
+    r32 = np.arange(8, dtype=np.float32)
+    g = r32.view(np.uint32).copy()
+    assert bench.compare_to_oracle(s, g, None, r32, None) == {"bitexact": True, "max_ulp": 0}
+    g[3] += 1
+    assert bench.compare_to_oracle(s, g, None, r32, None) == {"bitexact": False, "max_ulp": 1}
+
+
+def test_all_core_oracle_leg_matches_one_thread():
+    """The all-core leg splits rows (fused) or elements (sum) into blocks; the
+    result must be bitwise the one-thread result."""
+    import bench
+    from tensor_all_reduce_ar_amd import inputs
+    for w in (inputs.random_fused("fp16", 3, 37, 640, 9), inputs.random_sum("bf16", 5, 10007, 9)):
+        o = bench.oracle_timed(w, 2, 2, 5.0)
+        assert o["nt_bitexact"] and o["n1"] == 2 and o["nn"] == 2 and o["threads"] >= 1
