@@ -307,7 +307,8 @@ def bench_slice(torch, ar, w, args, stream, num):
 def bench_small(torch, ar, w, stream, calls=20, reps=20):
     """A launch-bound workload on one set of buffers (warm in cache, as right
     after the GEMMs that produce the partials): per-call time of eager
-    back-to-back launches through the binding, and of a HIP graph of `calls`
+    back-to-back launches through the binding (each call marshalling its
+    arguments, and through a prepared call), and of a HIP graph of `calls`
     back-to-back calls replayed `reps` times (one per-call figure per replay),
     which takes the host's launch cost out. Returns the outputs of the last
     call as raw bits."""
@@ -334,6 +335,19 @@ def bench_small(torch, ar, w, stream, calls=20, reps=20):
     b.record(stream)
     torch.cuda.synchronize()
     eager = a.elapsed_time(b) * 1e3 / (calls * reps)
+    # the same, through a prepared call (argument block built once)
+    if w.op == "sum":
+        prep = ar.prepare_sum(parts, out)
+    else:
+        prep = ar.prepare_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res)
+    prep()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(calls * reps):
+        prep()
+    b.record(stream)
+    torch.cuda.synchronize()
+    eager_prepared = a.elapsed_time(b) * 1e3 / (calls * reps)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -353,7 +367,8 @@ def bench_small(torch, ar, w, stream, calls=20, reps=20):
     torch.cuda.synchronize()
     per_call = [x.elapsed_time(y) / calls for x, y in evs]  # ms
     del g
-    return dict(eager_us=eager, per_call=per_call, calls=calls, reps=reps, out_bits=host_bits(torch, out),
+    return dict(eager_us=eager, eager_prepared_us=eager_prepared, per_call=per_call, calls=calls, reps=reps,
+                out_bits=host_bits(torch, out),
                 inter_bits=host_bits(torch, inter) if inter is not None else None)
 
 
@@ -694,7 +709,8 @@ def main():
             stats = launch_stats(r["per_call"])
             stats["launches"] = r["calls"] * r["reps"]
             records[nm] = workload_record(sw_, sw_.algorithmic_bytes(), WARM, stats, {
-                "eager_us_per_call": round(r["eager_us"], 2), "graph_replays": r["reps"]})
+                "eager_us_per_call": round(r["eager_us"], 2),
+                "eager_prepared_us_per_call": round(r["eager_prepared_us"], 2), "graph_replays": r["reps"]})
             gpu[nm] = (sw_, r["out_bits"], r["inter_bits"])
         print("[bench] launch-bound workloads done", file=sys.stderr, flush=True)
 

@@ -17,8 +17,10 @@ Entry points, same names as the C ABI:
   ar_configuration_supported(params, fusion_op), ar_workspace_size(params),
   ar_partials_layout(elts_total, dtype, ranks), ar_status_string(code), ar_last_hip_error()
 plus ``allocate_workspace`` (one device allocation holding the R partials at
-the slots ar_partials_layout gives), and ``Params`` / ``make_params``, ``call``
-and ``call_slice`` for raw-pointer use.
+the slots ar_partials_layout gives), ``prepare_sum`` /
+``prepare_residual_rmsnorm`` (a call whose argument block is built and checked
+once, for loops that run the op on the same buffers again and again), and
+``Params`` / ``make_params``, ``call`` and ``call_slice`` for raw-pointer use.
 """
 from __future__ import annotations
 
@@ -324,3 +326,42 @@ def ar_residual_rmsnorm_slice(partials: Sequence, weight, eps: float, out, inter
     """Rows of slice `slice_index` of `num_slices` of ar_residual_rmsnorm, in place."""
     params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
     _run("ar_residual_rmsnorm_slice", params, stream, out.device, (slice_index, num_slices))
+
+
+class PreparedCall:
+    """One entry point bound to one set of buffers: the ar_params_t block is
+    built and the tensors checked once, when the call is prepared; each call
+    then only reads the current stream and calls the C entry point, whose own
+    validation still runs. The call keeps references to its tensors, so they
+    stay allocated while it exists. Raises ArError on a non-zero status."""
+
+    def __init__(self, fn: str, params: Params, device, tensors):
+        self.fn, self.params, self.device, self._keep = fn, params, device, tensors
+        self._c = getattr(load(), fn)
+        self._pp = ctypes.byref(params)
+        self._raw = None
+        import torch
+        self._raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        self._dev = getattr(torch._C, "_cuda_getDevice", None)
+
+    def __call__(self, stream=None) -> None:
+        idx = self.device.index
+        if stream is None and self._raw is not None and self._dev is not None and self._dev() == idx:
+            st = self._c(self._pp, ctypes.c_void_p(self._raw(idx)))
+            if st != AR_OK:
+                raise ArError(st, self.fn)
+            return
+        _run(self.fn, self.params, stream, self.device)
+
+
+def prepare_sum(partials: Sequence, out) -> PreparedCall:
+    """ar_sum on these buffers, ready to call: ``prepare_sum(parts, out)()``."""
+    return PreparedCall("ar_sum", _sum_params(partials, out), out.device, (list(partials), out))
+
+
+def prepare_residual_rmsnorm(partials: Sequence, weight, eps: float, out, intermediate, bias=None, residual=None,
+                             hidden_size: Optional[int] = None) -> PreparedCall:
+    """ar_residual_rmsnorm on these buffers, ready to call."""
+    params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
+    return PreparedCall("ar_residual_rmsnorm", params, out.device,
+                        (list(partials), weight, out, intermediate, bias, residual))

@@ -477,3 +477,51 @@ def test_calls_from_several_host_threads():
             check_fused(w, host_bits(bufs[0]), host_bits(bufs[1]))
         else:
             assert_bitexact(host_bits(bufs[0]), ref_sum(w), w.dtype, f"threaded {w.name}")
+
+
+# ------------------------------------------------------------ prepared calls
+@pytest.mark.parametrize("name", [inputs.SUM_FP32_R2_4x256, inputs.SUM_FP16_R2_1000003, inputs.FUSED_FP16_R8_16x4096,
+                                  inputs.fused_fp16_r2_5120_name(7)])
+def test_prepared_calls_match_the_oracle_on_repeat(name):
+    """A prepared call (argument block built once) run three times, on the
+    current stream and on a side stream, gives the oracle's result each time;
+    inputs are refreshed between calls so a stale launch would show."""
+    note(f"[prepared] {name}")
+    w = inputs.make(name)
+    parts = [dev(p, w.dtype) for p in w.partials]
+    out = Guarded(w.n, w.dtype)
+    if w.op == "sum":
+        call_ = ar.prepare_sum(parts, out.t)
+        ref = ref_sum(w)
+    else:
+        inter = Guarded(w.n, w.dtype)
+        call_ = ar.prepare_residual_rmsnorm(parts, dev(w.weight, w.dtype), w.eps, out.t, inter.t,
+                                            bias=dev(w.bias, w.dtype), residual=dev(w.residual, w.dtype))
+    side = torch.cuda.Stream()
+    for k in range(3):
+        out.t.zero_()
+        if w.op != "sum":
+            inter.t.zero_()
+        torch.cuda.synchronize()
+        if k == 2:
+            side.wait_stream(torch.cuda.current_stream())
+            call_(stream=side)
+            torch.cuda.current_stream().wait_stream(side)
+        else:
+            call_()
+        torch.cuda.synchronize()
+        out.check_guards()
+        if w.op == "sum":
+            assert_bitexact(host_bits(out.t), bits(ref), w.dtype, f"prepared sum, call {k}")
+        else:
+            inter.check_guards()
+            check_fused(w, host_bits(out.t), host_bits(inter.t))
+
+
+def test_prepared_call_reports_errors():
+    """The C entry point's validation still runs on every prepared call."""
+    # partial overlap of the output with a partial is rejected when the call runs
+    base = torch.zeros(2048, device="cuda", dtype=torch.float16)
+    c = ar.prepare_sum([base[:1024], base[1024:]], base[8:1032])
+    with pytest.raises(ar.ArError, match="AR_ERR_ALIAS"):
+        c()
