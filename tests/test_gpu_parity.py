@@ -115,6 +115,25 @@ def test_sum_sizes_and_tails(dtype, ranks):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("ranks", [2, 6])
+def test_sum_sizes_at_the_shape_switch(dtype, ranks):
+    """Calls below CUs x 1024 packs take 256-lane x 1-pack steps, larger ones
+    1024-pack steps (512 x 2 up to 5 ranks, 256 x 4 from 6); either way the
+    packs after the last full step and the tail elements form a unit of their
+    own. Sizes just below and above the switch, with and without a remainder
+    and a tail, against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    v = 4 if dtype == "fp32" else 8
+    switch = cus * 1024  # packs
+    for npacks, tail in ((switch - 1, 0), (switch - 1, v - 1), (switch, 0), (switch, 3), (switch + 77, 5),
+                         (switch + 1023, v - 1), (2 * switch + 1024, 0)):
+        n = npacks * v + tail
+        note(f"[parity] sum {dtype} R={ranks} n={n} (switch at {switch} packs)")
+        w = inputs.random_sum(dtype, ranks, n, 2000 + ranks + npacks % 101 + tail)
+        assert_bitexact(run_sum(w), ref_sum(w), dtype, f"sum {dtype} R={ranks} n={n}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_sum_unaligned_pointers(dtype):
     """Element-aligned but not 16-byte aligned buffers take the element-wise kernel."""
     for offs, oo in (([1, 0, 0], 0), ([0, 0, 0], 1), ([3, 1, 2], 3)):
