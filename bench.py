@@ -5,7 +5,11 @@
 One step = one ar_residual_rmsnorm call on the large fused workload: 8 bf16
 rank partials of [2048 tokens, 8192 hidden] summed in fp32, plus residual, then
 RMSNorm (eps 1e-5, no bias), writing the pre-norm sum and the normed output.
-Inputs are seeded synthetic data already resident in HBM. Steps rotate over
+Inputs are seeded synthetic data already resident in HBM. The partials sit
+where the all-reduce keeps them: in one allocation from allocate_workspace
+(the slots of ar_partials_layout, the counterpart of the comm-buffer workspace
+the pages' kernels read); --partials separate puts each in its own torch
+allocation instead, and the line reports that layout beside the headline. Steps rotate over
 enough copies of the inputs and outputs (at least 4x the 256 MB last-level
 cache in all, the outputs alone at least 2x) that each call streams from and
 to HBM rather than the cache.
@@ -23,6 +27,7 @@ reported too.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -52,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the unfused and two-shot line items")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (repeats the sample)")
+    ap.add_argument("--partials", choices=("workspace", "separate"), default="workspace",
+                    help="where the headline's rank partials live: one allocation from allocate_workspace (the "
+                         "all-reduce workspace layout) or one torch allocation each")
     ap.add_argument("--min-calls", type=int, default=MIN_TIMED_CALLS,
                     help="calls timed for every workload but the headline (which takes --steps)")
     return ap.parse_args()
@@ -95,19 +103,24 @@ def time_launches(torch, launch, nsets, steps, warmup, stream):
         launch(i % nsets)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        launch(i % nsets)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    region_ms = start.elapsed_time(stop)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        launch(i % nsets)
-        b.record(stream)
-    torch.cuda.synchronize()
-    return region_ms / steps, [a.elapsed_time(b) for a, b in evs]
+    gc_was_on = gc.isenabled()
+    gc.disable()  # no collector pause while the host queues a timed region
+    try:
+        start.record(stream)
+        for i in range(steps):
+            launch(i % nsets)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            launch(i % nsets)
+            b.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        if gc_was_on:
+            gc.enable()
+    return start.elapsed_time(stop) / steps, [a.elapsed_time(b) for a, b in evs]
 
 
 OUTLIER_FACTOR = 1.5
@@ -143,6 +156,22 @@ def slab_copies(torch, ar, parts):
     return ws.buffer, ws.partials
 
 
+def partial_sets(torch, ar, base, nsets, layout):
+    """`nsets` copies of the device partials `base` (set 0 may be `base`
+    itself): one allocation per partial ("separate"), or all partials of a set
+    in one allocation from allocate_workspace ("slab"). Returns the sets and
+    the allocations to keep alive."""
+    sets, keep = [], []
+    for k in range(nsets):
+        if layout == "slab":
+            slab, parts = slab_copies(torch, ar, base)
+            keep.append(slab)
+        else:
+            parts = base if k == 0 else [p.clone() for p in base]
+        sets.append(parts)
+    return sets, keep
+
+
 def bench_fused(torch, ar, w, args, stream, layout="separate"):
     """layout: "separate" (one allocation per partial) or "slab" (the partials
     of a set in one allocation at ar_partials_layout's slots)."""
@@ -152,21 +181,20 @@ def bench_fused(torch, ar, w, args, stream, layout="separate"):
     res0 = dev(torch, w.residual, w.dtype)
     weight = dev(torch, w.weight, w.dtype)
     bias = dev(torch, w.bias, w.dtype) if w.bias is not None else None
-    sets, keep = [], []
+    psets, keep = partial_sets(torch, ar, base, nsets, layout)
+    sets = []
     for k in range(nsets):
-        if layout == "slab":
-            slab, parts = slab_copies(torch, ar, base)
-            keep.append(slab)
-        else:
-            parts = base if k == 0 else [p.clone() for p in base]
         res = res0 if k == 0 else res0.clone()
-        sets.append((parts, res, torch.empty_like(res0), torch.empty_like(res0)))
-    if layout == "slab":
-        del base
+        sets.append((psets[k], res, torch.empty_like(res0), torch.empty_like(res0)))
+    del base
+
+    # prepared calls: the host queues each launch in a few microseconds, far
+    # ahead of the device, so the timed region measures the kernels
+    preps = [ar.prepare_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res)
+             for parts, res, out, inter in sets]
 
     def launch(k):
-        parts, res, out, inter = sets[k]
-        ar.ar_residual_rmsnorm(parts, weight, w.eps, out, inter, bias=bias, residual=res, stream=stream)
+        preps[k](stream)
 
     ms_step, per = time_launches(torch, launch, nsets, args.steps, args.warmup, stream)
     out_bits, inter_bits = host_bits(torch, sets[0][2]), host_bits(torch, sets[0][3])
@@ -188,19 +216,14 @@ def bench_sum(torch, ar, w, args, stream, layout="separate"):
     nb = w.algorithmic_bytes()
     nsets = rotation_sets(nb, w.n * w.itemsize)
     base = [dev(torch, p, w.dtype) for p in w.partials]
-    sets, keep = [], []
-    for k in range(nsets):
-        if layout == "slab":
-            slab, parts = slab_copies(torch, ar, base)
-            keep.append(slab)
-        else:
-            parts = base if k == 0 else [p.clone() for p in base]
-        sets.append((parts, torch.empty_like(base[0])))
-    if layout == "slab":
-        del base
+    psets, keep = partial_sets(torch, ar, base, nsets, layout)
+    sets = [(psets[k], torch.empty_like(base[0])) for k in range(nsets)]
+    del base
+
+    preps = [ar.prepare_sum(parts, out) for parts, out in sets]
 
     def launch(k):
-        ar.ar_sum(sets[k][0], sets[k][1], stream=stream)
+        preps[k](stream)
 
     steps = max(args.min_calls, args.steps)
     ms_step, per = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
@@ -213,7 +236,7 @@ def bench_sum(torch, ar, w, args, stream, layout="separate"):
                 ceil=ceil)
 
 
-def bench_unfused(torch, ar, w, args, stream):
+def bench_unfused(torch, ar, w, args, stream, layout="separate"):
     """The unfused path on the fused workload: ar_sum into a buffer X, then
     ar_rmsnorm (residual, bias, norm) on X. Bytes: the sum's (R+1)*N*s, the
     norm's (X + residual + S + out)*N*s plus weight (and bias)."""
@@ -225,23 +248,25 @@ def bench_unfused(torch, ar, w, args, stream):
     res0 = dev(torch, w.residual, w.dtype)
     weight = dev(torch, w.weight, w.dtype)
     bias = dev(torch, w.bias, w.dtype) if w.bias is not None else None
+    psets, keep = partial_sets(torch, ar, base, nsets, layout)
     sets = []
     for k in range(nsets):
-        parts = base if k == 0 else [p.clone() for p in base]
         res = res0 if k == 0 else res0.clone()
-        sets.append((parts, res, torch.empty_like(res0), torch.empty_like(res0), torch.empty_like(res0)))
+        sets.append((psets[k], res, torch.empty_like(res0), torch.empty_like(res0), torch.empty_like(res0)))
+
+    preps = [(ar.prepare_sum(parts, x), ar.prepare_rmsnorm(x, weight, w.eps, out, inter, bias=bias, residual=res))
+             for parts, res, x, out, inter in sets]
 
     def launch(k):
-        parts, res, x, out, inter = sets[k]
-        ar.ar_sum(parts, x, stream=stream)
-        ar.ar_rmsnorm(x, weight, w.eps, out, inter, bias=bias, residual=res, stream=stream)
+        preps[k][0](stream)
+        preps[k][1](stream)
 
     steps = max(args.min_calls, args.steps)
     ms_step, _ = time_launches(torch, launch, nsets, steps, max(2, args.warmup // 2), stream)
     return dict(bytes=nb, nsets=nsets, ms_step=ms_step, steps=steps)
 
 
-def bench_slice(torch, ar, w, args, stream, num):
+def bench_slice(torch, ar, w, args, stream, num, layout="separate"):
     """One rank's share (slice 0 of `num`) of the two-shot split."""
     s = w.itemsize
     base = [dev(torch, p, w.dtype) for p in w.partials]
@@ -263,9 +288,10 @@ def bench_slice(torch, ar, w, args, stream, num):
     # rotate by the bytes the share itself touches (inputs and outputs), so
     # that its sets, not just the full buffers, exceed the cache as required
     nsets = rotation_sets(nb, (1 if w.op == "sum" else 2) * m * s)
-    sets = [(base, res0, out0, inter0)]
+    psets, keep = partial_sets(torch, ar, base, nsets, layout)
+    sets = [(psets[0], res0, out0, inter0)]
     for k in range(1, nsets):
-        sets.append(([p.clone() for p in base], res0.clone() if res0 is not None else None,
+        sets.append((psets[k], res0.clone() if res0 is not None else None,
                      torch.empty_like(base[0]), torch.empty_like(base[0])))
 
     def launch(k, on=None):
@@ -572,18 +598,24 @@ def main():
         raise SystemExit("--workload must name a fused workload")
     print(f"[bench] inputs for {name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    f = bench_fused(torch, ar, w, args, stream)
+    # The rank partials of the headline live where the all-reduce's own
+    # workspace puts them (allocate_workspace, the counterpart of the comm
+    # buffers the kernels read), unless --partials separate.
+    head_layout = "slab" if args.partials == "workspace" else "separate"
+    other_layout = "separate" if head_layout == "slab" else "slab"
+    f = bench_fused(torch, ar, w, args, stream, layout=head_layout)
     gbps = f["bytes"] / (f["ms_step"] * 1e-3) / 1e9
     # One launch per step, back to back on one stream (no gaps between them):
     # the region time per step is the average launch duration.
     achieved = gbps
-    print(f"[bench] fused: {f['ms_step'] * 1e3:.1f} us/step ({achieved:.0f} GB/s); isolated launches median "
+    print(f"[bench] fused ({args.partials} partials): {f['ms_step'] * 1e3:.1f} us/step ({achieved:.0f} GB/s); "
+          f"isolated launches median "
           f"{f['per']['median']:.1f} us; streaming ceiling on the same buffers {f['ceil']['gbps']:.0f} GB/s",
           file=sys.stderr, flush=True)
     gpu = {name: (w, f.pop("out_bits"), f.pop("inter_bits"))}  # outputs to check against the oracle
     records = {name: workload_record(w, f["bytes"], COLD, f["per"], {
         "us_per_call_back_to_back": round(f["ms_step"] * 1e3, 2), "rotating_input_sets": f["nsets"],
-        "stream_ceiling_same_buffers_gbps": f["ceil"]["gbps"]})}
+        "stream_ceiling_same_buffers_gbps": f["ceil"]["gbps"], "partials": args.partials})}
 
     result = {
         "metric": METRIC,
@@ -602,6 +634,8 @@ def main():
             "workload": name, "op": "RESIDUAL_RMS_NORM", "ranks": w.ranks, "tokens": w.rows,
             "hidden": w.hidden, "bias": w.bias is not None, "residual": w.residual is not None, "eps": w.eps,
             "bytes_per_step": f["bytes"], "rotating_input_sets": f["nsets"], "seeds": w.seeds,
+            "partials": ("one allocation per set from allocate_workspace (ar_partials_layout's staggered slots)"
+                         if head_layout == "slab" else "one torch allocation per partial"),
             "distribution": "normal(mean, variance): partials N(0,1/R), residual N(0,1), weight N(1,0.1)",
         },
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -647,16 +681,16 @@ def main():
         print(f"[bench] sum: {s['ms_step'] * 1e3:.1f} us/call ({s_ach:.0f} GB/s)", file=sys.stderr, flush=True)
 
     if not args.no_next:
-        u = bench_unfused(torch, ar, w, args, stream)
+        u = bench_unfused(torch, ar, w, args, stream, layout=head_layout)
         result["unfused_baseline"] = {
-            "what": "ar_sum into a buffer, then ar_rmsnorm on it (two launches)",
+            "what": "ar_sum into a buffer, then ar_rmsnorm on it (two launches), partials laid out as the headline's",
             "us_per_call": round(u["ms_step"] * 1e3, 2), "bytes_per_call": u["bytes"], "steps": u["steps"],
             "gbps": round(u["bytes"] / (u["ms_step"] * 1e-3) / 1e9, 1),
             "fused_us_per_call": round(f["ms_step"] * 1e3, 2),
             "time_saved_by_fusion": round(1 - f["ms_step"] / u["ms_step"], 4),
         }
         print(f"[bench] unfused: {u['ms_step'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
-        sl = bench_slice(torch, ar, w, args, stream, w.ranks)
+        sl = bench_slice(torch, ar, w, args, stream, w.ranks, layout=head_layout)
         result["two_shot_share"] = {
             "what": f"slice 0 of {w.ranks} of the fused op (one rank's share of a two-shot split)",
             "elements": sl["elements"], "bytes_per_call": sl["bytes"], "us_per_call": round(sl["ms_step"] * 1e3, 2),
@@ -668,19 +702,21 @@ def main():
               f"from a HIP graph", file=sys.stderr, flush=True)
 
         gpu_out, gpu_inter = gpu[name][1], gpu[name][2]
-        sl = bench_fused(torch, ar, w, args, stream, layout="slab")
+        sl = bench_fused(torch, ar, w, args, stream, layout=other_layout)
         sl_gbps = sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9
-        result["fused_partials_in_layout"] = {
-            "what": "the same fused workload with each set's partials in one allocation from allocate_workspace "
-                    "(the slots of ar_partials_layout: 4 KiB more stagger per partial)",
+        key = "fused_partials_separate" if other_layout == "separate" else "fused_partials_in_layout"
+        result[key] = {
+            "what": ("the same fused workload with one torch allocation per partial" if other_layout == "separate"
+                     else "the same fused workload with each set's partials in one allocation from "
+                          "allocate_workspace (the slots of ar_partials_layout: 4 KiB more stagger per partial)"),
             "us_per_call": round(sl["ms_step"] * 1e3, 2), "gbps": round(sl_gbps, 1),
             "frac": round(sl_gbps / HBM_PEAK_GBPS, 4), "isolated_launch_us": sl["per"],
             "stream_ceiling_same_buffers": sl["ceil"],
             "frac_of_stream_ceiling": round(sl_gbps / sl["ceil"]["gbps"], 4),
-            "gpu_matches_separate_layout": bool(np.array_equal(sl["out_bits"], gpu_out) and
+            "gpu_matches_headline_layout": bool(np.array_equal(sl["out_bits"], gpu_out) and
                                                 np.array_equal(sl["inter_bits"], gpu_inter)),
         }
-        print(f"[bench] fused, partials in ar_partials_layout slots: {sl['ms_step'] * 1e3:.1f} us/call "
+        print(f"[bench] fused, partials {other_layout}: {sl['ms_step'] * 1e3:.1f} us/call "
               f"({sl_gbps:.0f} GB/s)", file=sys.stderr, flush=True)
         del sl
         mw = inputs.make(inputs.fused_fp16_r2_5120_name(4096))

@@ -18,7 +18,7 @@ Entry points, same names as the C ABI:
   ar_partials_layout(elts_total, dtype, ranks), ar_status_string(code), ar_last_hip_error()
 plus ``allocate_workspace`` (one device allocation holding the R partials at
 the slots ar_partials_layout gives), ``prepare_sum`` /
-``prepare_residual_rmsnorm`` (a call whose argument block is built and checked
+``prepare_residual_rmsnorm`` / ``prepare_rmsnorm`` (a call whose argument block is built and checked
 once, for loops that run the op on the same buffers again and again), and
 ``Params`` / ``make_params``, ``call`` and ``call_slice`` for raw-pointer use.
 """
@@ -346,8 +346,12 @@ class PreparedCall:
 
     def __call__(self, stream=None) -> None:
         idx = self.device.index
-        if stream is None and self._raw is not None and self._dev is not None and self._dev() == idx:
-            st = self._c(self._pp, ctypes.c_void_p(self._raw(idx)))
+        if self._dev is not None and self._dev() == idx:
+            if stream is None and self._raw is not None:
+                h = self._raw(idx)
+            else:
+                h = _stream_handle(stream, self.device)
+            st = self._c(self._pp, ctypes.c_void_p(h))
             if st != AR_OK:
                 raise ArError(st, self.fn)
             return
@@ -365,3 +369,10 @@ def prepare_residual_rmsnorm(partials: Sequence, weight, eps: float, out, interm
     params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
     return PreparedCall("ar_residual_rmsnorm", params, out.device,
                         (list(partials), weight, out, intermediate, bias, residual))
+
+
+def prepare_rmsnorm(x, weight, eps: float, out, intermediate, bias=None, residual=None,
+                    hidden_size: Optional[int] = None) -> PreparedCall:
+    """ar_rmsnorm (the unfused path's norm step) on these buffers, ready to call."""
+    params = _fused_params([x], weight, eps, out, intermediate, bias, residual, hidden_size)
+    return PreparedCall("ar_rmsnorm", params, out.device, (x, weight, out, intermediate, bias, residual))

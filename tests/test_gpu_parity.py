@@ -544,3 +544,26 @@ def test_prepared_call_reports_errors():
     c = ar.prepare_sum([base[:1024], base[1024:]], base[8:1032])
     with pytest.raises(ar.ArError, match="AR_ERR_ALIAS"):
         c()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_prepared_unfused_path_matches_plain_calls(dtype):
+    """prepare_sum then prepare_rmsnorm (the unfused path, prepared) give
+    bitwise what ar_sum then ar_rmsnorm give, with and without side streams."""
+    note(f"[prepared] unfused {dtype}")
+    w = inputs.random_fused(dtype, 4, 37, 2560, 77)
+    parts = [dev(p, dtype) for p in w.partials]
+    wt, b, q = dev(w.weight, dtype), dev(w.bias, dtype), dev(w.residual, dtype)
+    x1, o1, s1 = (torch.empty_like(parts[0]) for _ in range(3))
+    ar.ar_sum(parts, x1)
+    ar.ar_rmsnorm(x1, wt, w.eps, o1, s1, bias=b, residual=q)
+    x2, o2, s2 = (torch.zeros_like(parts[0]) for _ in range(3))
+    ps, pn = ar.prepare_sum(parts, x2), ar.prepare_rmsnorm(x2, wt, w.eps, o2, s2, bias=b, residual=q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    ps(side)
+    pn(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for got, want, what in ((x2, x1, "sum"), (s2, s1, "intermediate"), (o2, o1, "output")):
+        assert_bitexact(host_bits(got), host_bits(want), dtype, f"prepared unfused {what}")
