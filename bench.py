@@ -9,7 +9,8 @@ Inputs are seeded synthetic data already resident in HBM. The partials sit
 where the all-reduce keeps them: in one allocation from allocate_workspace
 (the slots of ar_partials_layout, the counterpart of the comm-buffer workspace
 the pages' kernels read); --partials separate puts each in its own torch
-allocation instead, and the line reports that layout beside the headline. Steps rotate over
+allocation instead, and the line reports that layout beside the headline.
+The large sum and the fp16 2-rank fused workload take the same layout. Steps rotate over
 enough copies of the inputs and outputs (at least 4x the 256 MB last-level
 cache in all, the outputs alone at least 2x) that each call streams from and
 to HBM rather than the cache.
@@ -652,10 +653,10 @@ def main():
 
     if not args.no_sum:
         sw = inputs.make(inputs.SUM_BF16_R4_8192x8192)
-        s = bench_sum(torch, ar, sw, args, stream)
+        s = bench_sum(torch, ar, sw, args, stream, layout=head_layout)
         s_ach = s["bytes"] / (s["ms_step"] * 1e-3) / 1e9
         result["standalone_sum"] = {
-            "workload": sw.name, "kernel": SUM_KERNEL, "bytes_per_call": s["bytes"],
+            "workload": sw.name, "kernel": SUM_KERNEL, "bytes_per_call": s["bytes"], "partials": args.partials,
             "us_per_call": round(s["ms_step"] * 1e3, 2), "isolated_launch_us": s["per"],
             "gbps": round(s_ach, 1), "achieved": round(s_ach, 1),
             "frac": round(s_ach / HBM_PEAK_GBPS, 4), "steps": s["steps"], "rotating_input_sets": s["nsets"],
@@ -665,19 +666,20 @@ def main():
         }
         gpu[sw.name] = (sw, s.pop("out_bits"), None)
         if not args.no_next:
-            sl = bench_sum(torch, ar, sw, args, stream, layout="slab")
+            sl = bench_sum(torch, ar, sw, args, stream, layout=other_layout)
             sl_gbps = sl["bytes"] / (sl["ms_step"] * 1e-3) / 1e9
-            result["standalone_sum"]["partials_in_layout"] = {
-                "what": "the same sum with each set's partials in one allocation from allocate_workspace",
+            result["standalone_sum"]["other_partials_layout"] = {
+                "what": ("the same sum with one torch allocation per partial" if other_layout == "separate" else
+                         "the same sum with each set's partials in one allocation from allocate_workspace"),
                 "us_per_call": round(sl["ms_step"] * 1e3, 2), "gbps": round(sl_gbps, 1),
                 "frac": round(sl_gbps / HBM_PEAK_GBPS, 4), "stream_ceiling_same_buffers": sl["ceil"],
                 "frac_of_stream_ceiling": round(sl_gbps / sl["ceil"]["gbps"], 4),
-                "gpu_matches_separate_layout": bool(np.array_equal(sl["out_bits"], gpu[sw.name][1])),
+                "gpu_matches_headline_layout": bool(np.array_equal(sl["out_bits"], gpu[sw.name][1])),
             }
             del sl
         records[sw.name] = workload_record(sw, s["bytes"], COLD, s["per"], {
             "us_per_call_back_to_back": round(s["ms_step"] * 1e3, 2), "rotating_input_sets": s["nsets"],
-            "stream_ceiling_same_buffers_gbps": s["ceil"]["gbps"]})
+            "stream_ceiling_same_buffers_gbps": s["ceil"]["gbps"], "partials": args.partials})
         print(f"[bench] sum: {s['ms_step'] * 1e3:.1f} us/call ({s_ach:.0f} GB/s)", file=sys.stderr, flush=True)
 
     if not args.no_next:
@@ -720,10 +722,10 @@ def main():
               f"({sl_gbps:.0f} GB/s)", file=sys.stderr, flush=True)
         del sl
         mw = inputs.make(inputs.fused_fp16_r2_5120_name(4096))
-        m = bench_fused(torch, ar, mw, args, stream)
+        m = bench_fused(torch, ar, mw, args, stream, layout=head_layout)
         m_gbps = m["bytes"] / (m["ms_step"] * 1e-3) / 1e9
         result["fused_fp16_r2_4096x5120"] = {
-            "workload": mw.name, "kernel": FUSED_KERNEL, "bytes_per_call": m["bytes"],
+            "workload": mw.name, "kernel": FUSED_KERNEL, "bytes_per_call": m["bytes"], "partials": args.partials,
             "us_per_call": round(m["ms_step"] * 1e3, 2), "gbps": round(m_gbps, 1),
             "frac": round(m_gbps / HBM_PEAK_GBPS, 4), "rotating_input_sets": m["nsets"],
             "isolated_launch_us": m["per"], "traffic": measured_traffic(FUSED_KERNEL, mw.name),
@@ -733,7 +735,7 @@ def main():
         gpu[mw.name] = (mw, m.pop("out_bits"), m.pop("inter_bits"))
         records[mw.name] = workload_record(mw, m["bytes"], COLD, m["per"], {
             "us_per_call_back_to_back": round(m["ms_step"] * 1e3, 2), "rotating_input_sets": m["nsets"],
-            "stream_ceiling_same_buffers_gbps": m["ceil"]["gbps"]})
+            "stream_ceiling_same_buffers_gbps": m["ceil"]["gbps"], "partials": args.partials})
         print(f"[bench] fused fp16 R=2 4096x5120: {m['ms_step'] * 1e3:.1f} us/call ({m_gbps:.0f} GB/s)",
               file=sys.stderr, flush=True)
 
