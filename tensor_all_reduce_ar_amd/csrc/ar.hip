@@ -482,6 +482,25 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
     const u32x4 *weight = static_cast<const u32x4 *>(a.weight);
     const int T = blockDim.x;
 
+    // With one or two ranks a slot reads only 3-4 HBM streams, and the weight
+    // and bias packs (the same columns in every row) are 2 of its 5-6 loads:
+    // the pipelined layouts then load them once per workgroup instead of once
+    // per row. With more ranks they are a smaller share of the loads, and
+    // holding them across rows costs registers and so resident workgroups.
+    constexpr bool kHoist = MODE != kPlain && R <= 2;
+    u32x4 wh[kHoist ? PPT : 1], bh[kHoist ? PPT : 1];
+    if constexpr (kHoist) {
+        const bool last_ok = MODE == kFull || threadIdx.x + (PPT - 1) * T < a.ppr;
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            wh[p] = bh[p] = u32x4{0, 0, 0, 0};
+            if (p + 1 < PPT || last_ok) {
+                wh[p] = weight[threadIdx.x + p * T];
+                if (bias)
+                    bh[p] = bias[threadIdx.x + p * T];
+            }
+        }
+    }
     for (size_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const size_t row0 = row * static_cast<size_t>(a.ppr);
         u32x4 sp[PPT], w[PPT];
@@ -497,8 +516,14 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
                 if (p + 2 < PPT || (p + 1 < PPT && last_ok))
                     load_slot<R>(a, row0 + j + T, v[(p + 1) & 1], rq[(p + 1) & 1]);
                 if (p + 1 < PPT || last_ok) {
-                    const u32x4 bq = bias ? bias[j] : u32x4{0, 0, 0, 0};
-                    w[p] = weight[j];
+                    u32x4 bq;
+                    if constexpr (kHoist) {
+                        bq = bh[p];
+                        w[p] = wh[p];
+                    } else {
+                        bq = bias ? bias[j] : u32x4{0, 0, 0, 0};
+                        w[p] = weight[j];
+                    }
                     sp[p] = fused_pre_norm<E, R>(v[p & 1], bias != nullptr, bq, a.residual != nullptr, rq[p & 1]);
                     ss += sum_squares<E>(sp[p]);
                 }
