@@ -66,12 +66,22 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash() -> str:
+def source_hash(texts=None) -> str:
+    """Hash of the kernel source (csrc/ar.hip, csrc/fused_geometry.h,
+    include/ar.h) with comments and whitespace removed, so that it changes
+    when the code does and not when only a comment does."""
+    import re
+    if texts is None:
+        texts = []
+        for rel in ("tensor_all_reduce_ar_amd/csrc/ar.hip", "tensor_all_reduce_ar_amd/csrc/fused_geometry.h",
+                    "include/ar.h"):
+            with open(os.path.join(ROOT, rel)) as f:
+                texts.append(f.read())
     h = hashlib.sha256()
-    for rel in ("tensor_all_reduce_ar_amd/csrc/ar.hip", "tensor_all_reduce_ar_amd/csrc/fused_geometry.h",
-                "include/ar.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for t in texts:
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(" ".join(t.split()).encode())
     return h.hexdigest()[:16]
 
 

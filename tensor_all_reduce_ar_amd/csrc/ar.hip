@@ -25,9 +25,10 @@
 //    change it, and fp32 denormals are kept (the kernels' default mode);
 //  * the fused op runs one workgroup per row with the row held in registers:
 //    S is stored once it is formed, the sum of squares of the rounded S is
-//    reduced with cross-lane shuffles inside each 64-wide wave, then through
-//    LDS across waves with a single barrier, and the normed row is written
-//    from registers - each input is read once and each output written once;
+//    reduced across the 64 lanes of each wave with DPP lane moves (no LDS
+//    traffic), then through LDS across waves with a single barrier, and the
+//    normed row is written from registers - each input is read once and each
+//    output written once;
 //  * the workgroup shape follows the row width: whole power-of-two numbers of
 //    waves per workgroup where the width allows (the four SIMDs of a CU get
 //    equal shares), more lanes per row when there are too few rows to fill

@@ -73,3 +73,14 @@ def test_all_core_oracle_leg_matches_one_thread():
     for w in (inputs.random_fused("fp16", 3, 37, 640, 9), inputs.random_sum("bf16", 5, 10007, 9)):
         o = bench.oracle_timed(w, 2, 2, 5.0)
         assert o["nt_bitexact"] and o["n1"] == 2 and o["nn"] == 2 and o["threads"] >= 1
+
+
+def test_source_hash_follows_code_not_comments():
+    """The traffic figures in the bench line are tied to this hash: a comment
+    edit keeps it, any change to the code changes it."""
+    import bench
+    base = ["int f(int x) { return x + 1; } // one\n/* two */\n", "#define A 1\n", "x"]
+    h = bench.source_hash(base)
+    assert bench.source_hash(["int f(int x)  {\n return x + 1; }  // changed\n", "#define A 1 /* c */\n", "x"]) == h
+    assert bench.source_hash(["int f(int x) { return x + 2; }\n", "#define A 1\n", "x"]) != h
+    assert bench.source_hash(["int f(int x) { return x + 1; }\n", "#define A 2\n", "x"]) != h
