@@ -18,9 +18,10 @@ Entry points, same names as the C ABI:
   ar_partials_layout(elts_total, dtype, ranks), ar_status_string(code), ar_last_hip_error()
 plus ``allocate_workspace`` (one device allocation holding the R partials at
 the slots ar_partials_layout gives), ``prepare_sum`` /
-``prepare_residual_rmsnorm`` / ``prepare_rmsnorm`` (a call whose argument block is built and checked
-once, for loops that run the op on the same buffers again and again), and
-``Params`` / ``make_params``, ``call`` and ``call_slice`` for raw-pointer use.
+``prepare_residual_rmsnorm`` / ``prepare_rmsnorm`` (a call whose argument
+block is built and checked once, for loops that run the op on the same
+buffers again and again), and ``Params`` / ``make_params``, ``call`` and
+``call_slice`` for raw-pointer use.
 """
 from __future__ import annotations
 
@@ -333,13 +334,13 @@ class PreparedCall:
     built and the tensors checked once, when the call is prepared; each call
     then only reads the current stream and calls the C entry point, whose own
     validation still runs. The call keeps references to its tensors, so they
-    stay allocated while it exists. Raises ArError on a non-zero status."""
+    stay allocated while it exists; they must not be resized or re-pointed
+    (the block holds their addresses). Raises ArError on a non-zero status."""
 
     def __init__(self, fn: str, params: Params, device, tensors):
         self.fn, self.params, self.device, self._keep = fn, params, device, tensors
         self._c = getattr(load(), fn)
         self._pp = ctypes.byref(params)
-        self._raw = None
         import torch
         self._raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
         self._dev = getattr(torch._C, "_cuda_getDevice", None)

@@ -483,10 +483,10 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
     const u32x4 *weight = static_cast<const u32x4 *>(a.weight);
     const int T = blockDim.x;
 
-    // With one or two ranks a slot reads only 3-4 HBM streams, and the weight
-    // and bias packs (the same columns in every row) are 2 of its 5-6 loads:
-    // the pipelined layouts then load them once per workgroup instead of once
-    // per row. With more ranks they are a smaller share of the loads, and
+    // With one or two ranks a slot reads only 2-3 HBM streams (the partials
+    // and the residual), and the weight and bias packs (the same columns in
+    // every row) are 2 of its 4-5 loads: the pipelined layouts then load them
+    // once per workgroup instead of once per row. With more ranks they are a smaller share of the loads, and
     // holding them across rows costs registers and so resident workgroups.
     constexpr bool kHoist = MODE != kPlain && R <= 2;
     u32x4 wh[kHoist ? PPT : 1], bh[kHoist ? PPT : 1];
