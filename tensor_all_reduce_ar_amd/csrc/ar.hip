@@ -871,14 +871,19 @@ int resident_per_cu(K kernel, int threads, int dev, OccCache &cache)
 
 // The register-row kernel runs as one resident wave of workgroups (CUs x
 // workgroups per CU) that loop over the rows: no second dispatch round, whose
-// refill leaves CUs idle.
+// refill leaves CUs idle. Except at 3-5 ranks in the pipelined layouts on rows
+// of up to 1024 packs: there one workgroup per row, refilled by the hardware
+// as rows finish, measured 0.3-5.2 % faster (14 shapes, hidden 2560-8192 in
+// 16-bit types and 4096 in fp32), while at 8 ranks (the large workload), on
+// wider rows and at 2 ranks it was slower and at 6 mixed.
 template <class E, int R, int PPT, int BOUND, int MODE>
 void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
 {
     static OccCache occ;
     const size_t resident = static_cast<size_t>(cus) *
                             resident_per_cu(ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, MODE>, threads, dev, occ);
-    if (grid > resident)
+    const bool dispatched = MODE != kPlain && R >= 3 && R <= 5 && a.ppr <= 1024;
+    if (grid > resident && !dispatched)
         grid = static_cast<unsigned>(resident);
     hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, MODE>), dim3(grid), dim3(threads), 0, stream, a);
 }
