@@ -3,15 +3,17 @@
  *
  * Measurement only, not part of the all-reduce path. One call reads n_in
  * buffers and writes n_out buffers of the same size once each, with plain
- * streaming code: 16-byte non-temporal loads, a workgroup of `lanes` lanes
- * covering lanes x packs 16-byte packs of every buffer per step, consecutive
- * steps on consecutive workgroups. Stores are 16-byte non-temporal global
- * stores, or (the *_SC1 shapes) 16-byte buffer stores at device scope
- * (cache-policy field sc1, temporal). Timing it in each shape on the very
- * buffers an all-reduce call uses (same sizes, same addresses, same numbers
- * of read and write streams) and keeping the fastest gives the practical HBM
- * ceiling of that call, next to the 8 TB/s peak. No one shape or store form is
- * fastest for every mix of streams.
+ * streaming code: a workgroup of `lanes` lanes covering lanes x packs 16-byte
+ * packs of every buffer per step, consecutive steps on consecutive
+ * workgroups. Loads are 16-byte non-temporal global loads, or (the *_BL
+ * shapes) 16-byte non-temporal buffer loads from the step's start address.
+ * Stores are 16-byte non-temporal global stores, or (the *_SC1 shapes)
+ * 16-byte buffer stores at device scope (cache-policy field sc1, temporal).
+ * Timing it in each shape on the very buffers an all-reduce call uses (same
+ * sizes, same addresses, same numbers of read and write streams) and keeping
+ * the fastest gives the practical HBM ceiling of that call, next to the
+ * 8 TB/s peak. No one shape, load form or store form is fastest for every mix
+ * of streams.
  *
  * What it computes, per 16-byte pack i:
  *     x = in[0][i] ^ in[1][i] ^ ... ^ in[n_in-1][i]      (bitwise, as 4 x u32)
@@ -40,17 +42,20 @@ extern "C" {
 #define SC_MAX_IN 12
 #define SC_MAX_OUT 2
 
-/* Workgroup shapes: lanes x packs per lane per step; _SC1: device-scope buffer stores. */
+/* Workgroup shapes: lanes x packs per lane per step (0-3), plus SC_SHAPE_SC1
+ * for device-scope buffer stores and SC_SHAPE_BL for buffer loads. */
 enum {
     SC_SHAPE_512x2 = 0,
     SC_SHAPE_256x4 = 1,
     SC_SHAPE_256x8 = 2,
     SC_SHAPE_128x8 = 3,
+    SC_SHAPE_SC1 = 4,
+    SC_SHAPE_BL = 8,
     SC_SHAPE_512x2_SC1 = 4,
     SC_SHAPE_256x4_SC1 = 5,
     SC_SHAPE_256x8_SC1 = 6,
     SC_SHAPE_128x8_SC1 = 7,
-    SC_NUM_SHAPES = 8
+    SC_NUM_SHAPES = 16
 };
 
 enum {

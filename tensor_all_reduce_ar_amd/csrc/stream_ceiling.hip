@@ -1,11 +1,14 @@
 // stream_ceiling.hip - streaming-ceiling kernels for gfx950 (measurement only;
 // C ABI in stream_ceiling.h). Each call reads NI buffers and writes NO buffers
-// of the same size once, 16-byte non-temporal loads, in one of a few
-// workgroup shapes (lanes x packs per lane per step) and one of two store
-// forms, with no other work: non-temporal global stores, or buffer stores at
-// device scope (cache-policy field sc1) from the step's start address. No
-// single shape or store form is fastest for every mix of streams, so a caller
-// times each.
+// of the same size once, with no other work, in one of a few workgroup shapes
+// (lanes x packs per lane per step), one of two load forms and one of two
+// store forms. Loads are 16-byte and non-temporal: global loads from 64-bit
+// per-lane addresses, or buffer loads from the step's start address (a
+// workgroup-uniform resource and a 32-bit lane offset, which leaves far more
+// registers free and so more waves resident). Stores are non-temporal global
+// stores, or buffer stores at device scope (cache-policy field sc1) from the
+// step's start address. No single variant is fastest for every mix of
+// streams, so a caller times each.
 
 #include <hip/hip_runtime.h>
 
@@ -41,6 +44,16 @@ __device__ __forceinline__ void one_pack(const StreamArgs &a, size_t j)
 
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) 32-bit data format
 constexpr int kPolicySc1 = 16;            // cache-policy field: sc1 (device scope), temporal
+constexpr int kPolicyNt = 2;              // cache-policy field: nt (non-temporal)
+
+// Pack at byte offset `off` of the `extent` bytes from `base` (the same in
+// every lane of the wave), non-temporal.
+__device__ __forceinline__ u32x4 load_buf(const u32x4 *base, uint32_t off, uint32_t extent)
+{
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4 *>(base), 0, static_cast<int>(extent), kBufferWord3);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kPolicyNt);
+}
 
 // Pack at byte offset `off` of the `extent` bytes from `base`; `base` is the
 // same in every lane of the wave.
@@ -50,10 +63,21 @@ __device__ __forceinline__ void store_sc1(u32x4 *base, uint32_t off, uint32_t ex
     __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kPolicySc1);
 }
 
+// Pack `base + u * kThreads` of input r in a full step that starts at pack
+// `c * step`: a global load, or (BL) a buffer load from the step's start.
+template <int kThreads, bool BL>
+__device__ __forceinline__ u32x4 step_load(const u32x4 *in, size_t c, size_t step, size_t base, int u)
+{
+    if (BL)
+        return load_buf(in + c * step, (threadIdx.x + u * kThreads) * 16u, static_cast<uint32_t>(step * 16u));
+    return __builtin_nontemporal_load(in + base + u * kThreads);
+}
+
 // kThreads lanes x kUnroll packs per step; consecutive steps go to
 // consecutive workgroups; the packs after the last full step are done by the
-// last workgroup. SC1: the full steps' stores are device-scope buffer stores.
-template <int NI, int NO, int kThreads, int kUnroll, bool SC1>
+// last workgroup. SC1: the full steps' stores are device-scope buffer stores;
+// BL: the full steps' loads are buffer loads.
+template <int NI, int NO, int kThreads, int kUnroll, bool SC1, bool BL>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a)
 {
     const size_t step = static_cast<size_t>(kThreads) * kUnroll;
@@ -63,12 +87,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a)
         u32x4 x[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            x[u] = __builtin_nontemporal_load(a.in[0] + base + u * kThreads);
+            x[u] = step_load<kThreads, BL>(a.in[0], c, step, base, u);
 #pragma unroll
         for (int r = 1; r < NI; ++r)
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                x[u] ^= __builtin_nontemporal_load(a.in[r] + base + u * kThreads);
+                x[u] ^= step_load<kThreads, BL>(a.in[r], c, step, base, u);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
@@ -87,28 +111,36 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a)
             one_pack<NI, NO>(a, j);
 }
 
-template <int NI, int NO, int T, int U, bool SC1>
+template <int NI, int NO, int T, int U, bool SC1, bool BL>
 int32_t launch(const StreamArgs &a, hipStream_t stream)
 {
     size_t blocks = a.npacks / (static_cast<size_t>(T) * U);
     const unsigned grid = blocks < 1 ? 1u : blocks > kMaxGrid ? kMaxGrid : static_cast<unsigned>(blocks);
-    hipLaunchKernelGGL((stream_kernel<NI, NO, T, U, SC1>), dim3(grid), dim3(T), 0, stream, a);
+    hipLaunchKernelGGL((stream_kernel<NI, NO, T, U, SC1, BL>), dim3(grid), dim3(T), 0, stream, a);
     return hipGetLastError() == hipSuccess ? SC_OK : SC_ERR_HIP;
+}
+
+// Shapes 0-3: the workgroup geometry; + SC_SHAPE_SC1: sc1 buffer stores;
+// + SC_SHAPE_BL: buffer loads.
+template <int NI, int NO, bool SC1, bool BL>
+int32_t by_geometry(int geometry, const StreamArgs &a, hipStream_t s)
+{
+    switch (geometry) {
+    case SC_SHAPE_512x2: return launch<NI, NO, 512, 2, SC1, BL>(a, s);
+    case SC_SHAPE_256x4: return launch<NI, NO, 256, 4, SC1, BL>(a, s);
+    case SC_SHAPE_256x8: return launch<NI, NO, 256, 8, SC1, BL>(a, s);
+    default: return launch<NI, NO, 128, 8, SC1, BL>(a, s);
+    }
 }
 
 template <int NI, int NO>
 int32_t by_shape(int shape, const StreamArgs &a, hipStream_t s)
 {
-    switch (shape) {
-    case SC_SHAPE_512x2: return launch<NI, NO, 512, 2, false>(a, s);
-    case SC_SHAPE_256x4: return launch<NI, NO, 256, 4, false>(a, s);
-    case SC_SHAPE_256x8: return launch<NI, NO, 256, 8, false>(a, s);
-    case SC_SHAPE_128x8: return launch<NI, NO, 128, 8, false>(a, s);
-    case SC_SHAPE_512x2_SC1: return launch<NI, NO, 512, 2, true>(a, s);
-    case SC_SHAPE_256x4_SC1: return launch<NI, NO, 256, 4, true>(a, s);
-    case SC_SHAPE_256x8_SC1: return launch<NI, NO, 256, 8, true>(a, s);
-    default: return launch<NI, NO, 128, 8, true>(a, s);
-    }
+    const int geometry = shape % SC_SHAPE_SC1;
+    const bool sc1 = shape & SC_SHAPE_SC1, bl = shape & SC_SHAPE_BL;
+    if (bl)
+        return sc1 ? by_geometry<NI, NO, true, true>(geometry, a, s) : by_geometry<NI, NO, false, true>(geometry, a, s);
+    return sc1 ? by_geometry<NI, NO, true, false>(geometry, a, s) : by_geometry<NI, NO, false, false>(geometry, a, s);
 }
 
 template <int NO>

@@ -16,9 +16,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstream_c
 SC_MAX_IN, SC_MAX_OUT = 12, 2
 SC_OK = 0
 # SC_SHAPE_* of include/stream_ceiling.h: lanes x packs per lane per step;
-# "/sc1": device-scope buffer stores instead of non-temporal global stores
-SHAPES = {0: "512x2", 1: "256x4", 2: "256x8", 3: "128x8",
-          4: "512x2/sc1", 5: "256x4/sc1", 6: "256x8/sc1", 7: "128x8/sc1"}
+# "/sc1": device-scope buffer stores instead of non-temporal global stores;
+# "/bl": non-temporal buffer loads instead of non-temporal global loads
+_GEOMETRIES = ("512x2", "256x4", "256x8", "128x8")
+SHAPES = {g + s + b: _GEOMETRIES[g] + ("/sc1" if s else "") + ("/bl" if b else "")
+          for b in (0, 8) for s in (0, 4) for g in range(4)}
 
 _lib: Optional[ctypes.CDLL] = None
 

@@ -91,9 +91,12 @@ def test_vector_path_instructions(libar):
     assert "v_cvt_pk_f16_f32" in ops, "packed RNE conversion to fp16"
 
 
-def test_ceiling_store_forms(libceiling):
+def test_ceiling_load_and_store_forms(libceiling):
     asm, _ = libceiling
-    assert re.search(r"global_load_dwordx4 .* nt", asm), "16-byte non-temporal loads"
+    assert re.search(r"global_load_dwordx4 .* nt", asm), "16-byte non-temporal global loads"
+    bl = re.findall(r"buffer_load_dwordx4 .*", asm)
+    assert bl, "16-byte buffer loads"
+    assert all(re.search(r"\bnt\b", x) and not re.search(r"\b(sc0|sc1)\b", x) for x in bl), bl[:3]
     assert re.search(r"global_store_dwordx4 .* nt", asm), "16-byte non-temporal global stores"
     sc1 = re.findall(r"buffer_store_dwordx4 .*", asm)
     assert sc1, "16-byte buffer stores"

@@ -37,7 +37,7 @@ def test_negative_counts():
     assert sc.load().sc_stream(ins, -2, outs, 1, 1024, 0, None) == -1
 
 
-@pytest.mark.parametrize("shape", [-1, 8])
+@pytest.mark.parametrize("shape", [-1, 16])
 def test_bad_shape(shape):
     assert sc.sc_stream_raw([A], [A + 4096], 1024, shape) == -4
 
