@@ -74,6 +74,7 @@ class Workload:
     weight: Optional[np.ndarray] = None
     eps: float = 0.0
     seeds: Dict[str, int] = dataclasses.field(default_factory=dict)
+    distribution: str = ""  # how the values were drawn, for reports
 
     @property
     def rows(self) -> int:
@@ -102,8 +103,10 @@ def _sum_workload(name, dtype, ranks, n, hidden, seed0, dist) -> Workload:
             parts.append(uniform((n,), seed0 + r, -1.0, 1.0, dtype))
         else:
             parts.append(normal((n,), seed0 + r, 0.0, 1.0 / ranks, dtype))
-    return Workload(name, "sum", dtype, ranks, n, hidden, parts,
-                    seeds={"partials": seed0})
+    drawn = "uniform[lo, hi]: partials U[-1, 1]" if dist == "uniform" else \
+        f"normal(mean, variance): partials N(0, 1/{ranks})"
+    return Workload(name, "sum", dtype, ranks, n, hidden, parts, seeds={"partials": seed0},
+                    distribution=f"{drawn}, rounded to {dtype}")
 
 
 def _fused_workload(name, dtype, ranks, rows, hidden, seed0, seed_b, seed_q, seed_w, eps) -> Workload:
@@ -115,7 +118,10 @@ def _fused_workload(name, dtype, ranks, rows, hidden, seed0, seed_b, seed_q, see
     seeds = {"partials": seed0, "residual": seed_q, "weight": seed_w}
     if seed_b is not None:
         seeds["bias"] = seed_b
-    return Workload(name, "fused", dtype, ranks, n, hidden, parts, bias, residual, weight, eps, seeds)
+    drawn = f"partials N(0, 1/{ranks}), " + ("bias N(0, 0.02), " if seed_b is not None else "") + \
+        "residual N(0, 1), weight N(1, 0.1)"
+    return Workload(name, "fused", dtype, ranks, n, hidden, parts, bias, residual, weight, eps, seeds,
+                    f"normal(mean, variance): {drawn}, rounded to {dtype}")
 
 
 # The named workloads. Names say what each is: op, type, ranks, shape.

@@ -54,15 +54,19 @@ def test_comparison_rules_of_the_bench():
     got[1] = 0x0000           # -0 vs +0: 0 ulp
     got[2] = 0x8001           # smallest subnormals of either sign: 2 ulp apart
     rec = bench.compare_to_oracle(w, got, ref.copy(), ref, ref)
-    assert rec == {"intermediate_bitexact": True, "output_max_ulp": 2, "within_tolerance": True}
-    got[0] = 0x3F83           # 3 ulp
-    assert not bench.compare_to_oracle(w, got, ref.copy(), ref, ref)["within_tolerance"]
+    # relative error floored at the smallest normal: 2^-132 apart / 2^-126
+    assert rec == {"intermediate_bitexact": True, "output_max_ulp": 2, "output_max_rel": 2.0 ** -6,
+                   "within_tolerance": True}
+    got[0] = 0x3F83           # 3 ulp above 1.0
+    rec = bench.compare_to_oracle(w, got, ref.copy(), ref, ref)
+    assert not rec["within_tolerance"] and rec["output_max_rel"] == 3 * 2.0 ** -7
     s = inputs.random_sum("fp32", 2, 8, 5)
     r32 = np.arange(8, dtype=np.float32)
     g = r32.view(np.uint32).copy()
-    assert bench.compare_to_oracle(s, g, None, r32, None) == {"bitexact": True, "max_ulp": 0}
-    g[3] += 1
-    assert bench.compare_to_oracle(s, g, None, r32, None) == {"bitexact": False, "max_ulp": 1}
+    assert bench.compare_to_oracle(s, g, None, r32, None) == {"bitexact": True, "max_ulp": 0, "max_rel": 0.0}
+    g[3] += 1                 # one ulp above 3.0
+    assert bench.compare_to_oracle(s, g, None, r32, None) == {"bitexact": False, "max_ulp": 1,
+                                                              "max_rel": 2.0 ** -22 / 3}
 
 
 def test_all_core_oracle_leg_matches_one_thread():
