@@ -125,25 +125,17 @@ def ar_last_hip_error() -> int:
     return load().ar_last_hip_error()
 
 
+_PtrArray = ctypes.c_void_p * AR_MAX_RANKS
+
+
 def make_params(elts_total: int, ranks: int, dtype: int, inputs: Sequence[int], output: int,
                 hidden_size: int = 0, weight: int = 0, eps: float = 0.0, intermediate: int = 0,
                 bias: int = 0, residual: int = 0) -> Params:
-    """Fill an ar_params_t from raw device addresses (0 = NULL)."""
-    p = Params()
-    p.elts_total = elts_total
-    p.ranks = ranks
-    p.dtype = dtype
-    for r, ptr in enumerate(list(inputs)[:AR_MAX_RANKS]):
-        p.input_buffer_ptrs[r] = ptr or None
-    p.local_output_buffer_ptr = output or None
-    f = p.fusion_params
-    f.bias_buffer = bias or None
-    f.residual_buffer = residual or None
-    f.hidden_size = hidden_size
-    f.weight_buffer = weight or None
-    f.eps = eps
-    f.intermediate_buffer = intermediate or None
-    return p
+    """Fill an ar_params_t from raw device addresses (0 = NULL); entries of
+    `inputs` past AR_MAX_RANKS are ignored, missing ones are NULL."""
+    ptrs = _PtrArray(*[q or None for q in list(inputs)[:AR_MAX_RANKS]])
+    fusion = FusionParams(bias or None, residual or None, hidden_size, weight or None, eps, intermediate or None)
+    return Params(elts_total, ranks, dtype, ptrs, output or None, fusion)
 
 
 def call(fn: str, params: Params, stream: Optional[int] = None) -> int:
@@ -218,15 +210,28 @@ def allocate_workspace(elts_total: int, dtype, ranks: int, device=None) -> Works
 
 
 # ------------------------------------------------------------ torch front end
+_CODES = {}
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: AR_FP32, torch.float16: AR_FP16, torch.bfloat16: AR_BF16}
-    if t.dtype not in codes:
+    if not _CODES:
+        import torch
+        _CODES.update({torch.float32: AR_FP32, torch.float16: AR_FP16, torch.bfloat16: AR_BF16})
+    code = _CODES.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return codes[t.dtype]
+    return code
 
 
 def _check(t, name: str, dtype, numel: int, device=None):
+    """t.data_ptr() once t is a contiguous device tensor of `numel` elements
+    of `dtype` (on `device`, if given); raises otherwise. The usual case is
+    one chained test of cheap attributes; the messages are built only when it
+    fails."""
+    idx = t.get_device()  # -1 for a host tensor
+    if t.dtype is dtype and idx >= 0 and (device is None or idx == device.index) and t.numel() == numel \
+            and t.is_contiguous():
+        return t.data_ptr()
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if device is not None and t.device != device:
@@ -235,9 +240,7 @@ def _check(t, name: str, dtype, numel: int, device=None):
         raise ValueError(f"{name} must be contiguous")
     if t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if t.numel() != numel:
-        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
-    return t.data_ptr()
+    raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
 
 
 def _stream_handle(stream, device) -> int:
