@@ -537,6 +537,51 @@ def test_prepared_calls_match_the_oracle_on_repeat(name):
             check_fused(w, host_bits(out.t), host_bits(inter.t))
 
 
+def test_prepared_calls_replayed_from_a_graph():
+    """Prepared calls captured into a HIP graph (through torch's CUDA graph)
+    and replayed five times, with eager work between the replays (outputs
+    filled with NaN; before the last two, new partials copied into the same
+    buffers): every replay matches the oracle on the inputs it saw."""
+    note("[prepared] graph replay")
+    ws = [inputs.random_sum("bf16", 3, 70001, 1601), inputs.random_sum("bf16", 3, 70001, 1611)]
+    wf = [inputs.random_fused("fp16", 8, 24, 4096, 1602, bias=True),
+          inputs.random_fused("fp16", 8, 24, 4096, 1612, bias=True)]
+    sp = [dev(p, "bf16") for p in ws[0].partials]
+    fp = [dev(p, "fp16") for p in wf[0].partials]
+    wt, b, q = dev(wf[0].weight, "fp16"), dev(wf[0].bias, "fp16"), dev(wf[0].residual, "fp16")
+    so = torch.empty_like(sp[0])
+    fo, fi = torch.empty_like(fp[0]), torch.empty_like(fp[0])
+    calls = [ar.prepare_sum(sp, so), ar.prepare_residual_rmsnorm(fp, wt, wf[0].eps, fo, fi, bias=b, residual=q)]
+    for c in calls:  # warm up outside the capture
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for c in calls:
+                c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(5):
+        k = 0 if rep < 3 else 1
+        if rep == 3:  # same buffers, new contents (weight, bias and residual stay)
+            for t, p in zip(sp, ws[1].partials):
+                t.copy_(dev(p, "bf16"))
+            for t, p in zip(fp, wf[1].partials):
+                t.copy_(dev(p, "fp16"))
+        for t in (so, fo, fi):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitexact(host_bits(so), bits(ref_sum(ws[k])), "bf16", f"graph replay {rep}: sum")
+        w = inputs.Workload("graph-fused", "fused", "fp16", 8, wf[k].n, wf[k].hidden, wf[k].partials,
+                            wf[0].bias, wf[0].residual, wf[0].weight, wf[0].eps)
+        check_fused(w, host_bits(fo), host_bits(fi))
+
+
 def test_prepared_call_reports_errors():
     """The C entry point's validation still runs on every prepared call."""
     # partial overlap of the output with a partial is rejected when the call runs
