@@ -136,7 +136,7 @@ int32_t by_geometry(int geometry, const StreamArgs &a, hipStream_t s)
 template <int NI, int NO>
 int32_t by_shape(int shape, const StreamArgs &a, hipStream_t s)
 {
-    const int geometry = shape % SC_SHAPE_SC1;
+    const int geometry = shape & (SC_SHAPE_SC1 - 1);  // the low bits: SC_SHAPE_512x2 .. SC_SHAPE_128x8
     const bool sc1 = shape & SC_SHAPE_SC1, bl = shape & SC_SHAPE_BL;
     if (bl)
         return sc1 ? by_geometry<NI, NO, true, true>(geometry, a, s) : by_geometry<NI, NO, false, true>(geometry, a, s);
