@@ -173,6 +173,7 @@ def random_fused(dtype: str, ranks: int, rows: int, hidden: int, seed: int, eps:
                         seed + 100 if bias else None, seed + 101, seed + 102, eps)
     if not residual:
         w.residual = None
+        w.distribution = w.distribution.replace("residual N(0, 1), ", "")
     return w
 
 
