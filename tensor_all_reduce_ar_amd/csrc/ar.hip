@@ -61,7 +61,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kPackBytes = 16;
 using ar_geometry::FusedGeometry;
 using ar_geometry::kFull;
-using ar_geometry::kFullMaxPPT;
 using ar_geometry::kFusedMaxThreads;
 using ar_geometry::kMaxPPT;
 using ar_geometry::kPlain;
@@ -909,15 +908,24 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
 {
     if (threads < kWave || threads > BOUND || threads % kWave != 0 || PPT * threads < a.ppr)
         return false;
-    if constexpr (PPT >= 3 && PPT <= kFullMaxPPT) {
+    if constexpr (PPT >= 3) {
+        // fused_geometry gives 3..8 packs per lane only to rows that fill every
+        // slot, or (5..8 packs on 256 lanes) every slot but the last: the
+        // pipelined walks, the only ones compiled at this bound.
         switch (ar_geometry::pipeline_mode(PPT, threads, a.ppr)) {
         case kFull: launch_fused_pack_as<E, R, PPT, BOUND, kFull>(a, grid, threads, dev, cus, stream); return true;
-        case kRagged: launch_fused_pack_as<E, R, PPT, BOUND, kRagged>(a, grid, threads, dev, cus, stream); return true;
-        default: break;
+        case kRagged:
+            if constexpr (PPT >= 5) {
+                launch_fused_pack_as<E, R, PPT, BOUND, kRagged>(a, grid, threads, dev, cus, stream);
+                return true;
+            }
+            return false;
+        default: return false;
         }
+    } else {
+        launch_fused_pack_as<E, R, PPT, BOUND, kPlain>(a, grid, threads, dev, cus, stream);
+        return true;
     }
-    launch_fused_pack_as<E, R, PPT, BOUND, kPlain>(a, grid, threads, dev, cus, stream);
-    return true;
 }
 
 // Rows of 2049..4096 packs in 16-bit types: 512 lanes x PPT (5..8) packs in the

@@ -36,7 +36,7 @@ static bool instance_exists(int ppt, int bound, int mode, bool wide)
     if (bound == kWideRowLanes && ppt >= 5 && ppt <= kMaxPPT)
         return wide && (mode == kFull || mode == kRagged);
     if (bound == 256)
-        return ppt >= 3 && ppt <= kMaxPPT;
+        return ppt >= 3 && ppt <= kMaxPPT && (mode == kFull || (mode == kRagged && ppt >= 5));
     return false;
 }
 
