@@ -1020,11 +1020,8 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
             fprintf(stderr, "[ar] fused rows R=%d rows=%zu H=%d ppr=%d rows/iter=%d block=%d\n", R, a.rows, a.hidden,
                     a.ppr, g.rows, g.threads);
         bool ok = false;
-        switch (g.rows) {
-        case 2: ok = launch_fused_rows<E, R, 2>(a, g.threads, dev, cus, stream); break;
-        case 4: ok = launch_fused_rows<E, R, 4>(a, g.threads, dev, cus, stream); break;
-        default: break;
-        }
+        if (g.rows == 2)  // the one multi-row layout fused_geometry gives (rows of 512 packs)
+            ok = launch_fused_rows<E, R, 2>(a, g.threads, dev, cus, stream);
         if (!ok)
             return AR_ERR_SHAPE;  // unreachable: fused_geometry only yields shapes the kernel takes
     } else if (vec && g.ppt == 0) {
