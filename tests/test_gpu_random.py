@@ -20,7 +20,7 @@ from gpu_util import TORCH_DT, Guarded, assert_bitexact, assert_output_close, bi
 
 
 DTYPES = ("fp32", "fp16", "bf16")
-CASES = 120
+CASES = 600
 MAX_ELEMS = 1 << 21
 
 
