@@ -902,7 +902,8 @@ void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int de
 // 4 x 256 ragged on rows of 896 packs within 1 % of 2 x 448.
 // Returns false, launching nothing, if the shape does not fit the instance: a
 // workgroup larger than the launch bound would index `part` past its end and
-// exceed the registers the kernel was compiled for, and lanes must cover the row.
+// exceed the registers the kernel was compiled for, lanes must cover the row,
+// and at 3..8 packs per lane the row must take one of the compiled slot walks.
 template <class E, int R, int PPT, int BOUND>
 bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, int cus, hipStream_t stream)
 {
