@@ -14,7 +14,7 @@ import torch
 
 TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
 NP_DT = {"fp32": np.float32, "fp16": np.float16, "bf16": np.uint16}
-GUARD = 4096  # canary elements before and after each output
+GUARD_BYTES = 64 << 10  # canary bytes before and after each output
 
 
 def note(msg: str) -> None:
@@ -56,23 +56,24 @@ def empty_host(n: int, dtype: str) -> np.ndarray:
 
 
 class Guarded:
-    """A device buffer of n elements with GUARD canary elements on each side,
+    """A device buffer of n elements with GUARD_BYTES of canary on each side,
     filled with a fixed pattern, to catch writes out of bounds."""
     PATTERN16, PATTERN32 = 0x5A3C, 0x5A3C7E11
 
     def __init__(self, n: int, dtype: str, offset_elems: int = 0):
         self.n, self.dtype, self.offset = n, dtype, offset_elems
-        size = 2 * GUARD + n + offset_elems
+        self.guard = GUARD_BYTES // (4 if dtype == "fp32" else 2)
+        size = 2 * self.guard + n + offset_elems
         idt = torch.int32 if dtype == "fp32" else torch.int16
         pat = self.PATTERN32 if dtype == "fp32" else self.PATTERN16
         self.raw = torch.full((size,), pat, dtype=idt, device="cuda").view(TORCH_DT[dtype])
-        self.t = self.raw[GUARD + offset_elems:GUARD + offset_elems + n]
+        self.t = self.raw[self.guard + offset_elems:self.guard + offset_elems + n]
 
     def check_guards(self):
         b = host_bits(self.raw)
         pat = self.PATTERN32 if self.dtype == "fp32" else self.PATTERN16
-        lo = b[:GUARD + self.offset]
-        hi = b[GUARD + self.offset + self.n:]
+        lo = b[:self.guard + self.offset]
+        hi = b[self.guard + self.offset + self.n:]
         assert np.all(lo == pat) and np.all(hi == pat), "write outside the output buffer"
 
 
