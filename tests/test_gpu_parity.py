@@ -108,7 +108,7 @@ def test_golden_small_workloads():
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("ranks", range(1, 9))
 def test_sum_sizes_and_tails(dtype, ranks):
-    for n in (1, 7, 8, 9, 15, 16, 17, 1027, 2 * 256 * 8 + 5, 70001):
+    for n in (1, 7, 8, 9, 15, 16, 17, 1027, 2 * 256 * 8 + 5, 70001, 1_000_003):
         note(f"[parity] sum {dtype} R={ranks} n={n}")
         w = inputs.random_sum(dtype, ranks, n, 1000 + 10 * ranks + n % 97)
         assert_bitexact(run_sum(w), ref_sum(w), dtype, f"sum {dtype} R={ranks} n={n}")
