@@ -18,9 +18,10 @@ Entry points, same names as the C ABI:
   ar_partials_layout(elts_total, dtype, ranks), ar_status_string(code), ar_last_hip_error()
 plus ``allocate_workspace`` (one device allocation holding the R partials at
 the slots ar_partials_layout gives), ``prepare_sum`` /
-``prepare_residual_rmsnorm`` / ``prepare_rmsnorm`` (a call whose argument
-block is built and checked once, for loops that run the op on the same
-buffers again and again), and ``Params`` / ``make_params``, ``call`` and
+``prepare_residual_rmsnorm`` / ``prepare_rmsnorm`` and the slice forms
+``prepare_sum_slice`` / ``prepare_residual_rmsnorm_slice`` (a call whose
+argument block is built and checked once, for loops that run the op on the
+same buffers again and again), and ``Params`` / ``make_params``, ``call`` and
 ``call_slice`` for raw-pointer use.
 """
 from __future__ import annotations
@@ -340,8 +341,9 @@ class PreparedCall:
     stay allocated while it exists; they must not be resized or re-pointed
     (the block holds their addresses). Raises ArError on a non-zero status."""
 
-    def __init__(self, fn: str, params: Params, device, tensors):
+    def __init__(self, fn: str, params: Params, device, tensors, slice_args=None):
         self.fn, self.params, self.device, self._keep = fn, params, device, tensors
+        self._slice = tuple(slice_args) if slice_args is not None else None
         self._c = getattr(load(), fn)
         self._pp = ctypes.byref(params)
         import torch
@@ -355,11 +357,14 @@ class PreparedCall:
                 h = self._raw(idx)
             else:
                 h = _stream_handle(stream, self.device)
-            st = self._c(self._pp, ctypes.c_void_p(h))
+            if self._slice is None:
+                st = self._c(self._pp, ctypes.c_void_p(h))
+            else:
+                st = self._c(self._pp, self._slice[0], self._slice[1], ctypes.c_void_p(h))
             if st != AR_OK:
                 raise ArError(st, self.fn)
             return
-        _run(self.fn, self.params, stream, self.device)
+        _run(self.fn, self.params, stream, self.device, self._slice)
 
 
 def prepare_sum(partials: Sequence, out) -> PreparedCall:
@@ -373,6 +378,21 @@ def prepare_residual_rmsnorm(partials: Sequence, weight, eps: float, out, interm
     params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
     return PreparedCall("ar_residual_rmsnorm", params, out.device,
                         (list(partials), weight, out, intermediate, bias, residual))
+
+
+def prepare_sum_slice(partials: Sequence, out, slice_index: int, num_slices: int) -> PreparedCall:
+    """ar_sum_slice on these buffers and this slice, ready to call."""
+    return PreparedCall("ar_sum_slice", _sum_params(partials, out), out.device, (list(partials), out),
+                        (slice_index, num_slices))
+
+
+def prepare_residual_rmsnorm_slice(partials: Sequence, weight, eps: float, out, intermediate, slice_index: int,
+                                   num_slices: int, bias=None, residual=None,
+                                   hidden_size: Optional[int] = None) -> PreparedCall:
+    """ar_residual_rmsnorm_slice on these buffers and this slice, ready to call."""
+    params = _fused_params(partials, weight, eps, out, intermediate, bias, residual, hidden_size)
+    return PreparedCall("ar_residual_rmsnorm_slice", params, out.device,
+                        (list(partials), weight, out, intermediate, bias, residual), (slice_index, num_slices))
 
 
 def prepare_rmsnorm(x, weight, eps: float, out, intermediate, bias=None, residual=None,

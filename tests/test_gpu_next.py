@@ -144,6 +144,49 @@ def test_fused_slices_compose_to_the_full_op(dtype, num):
     assert np.array_equal(host_bits(out.t), host_bits(full_out))
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_prepared_slices_match_the_plain_slices(dtype):
+    """Prepared slice calls (one per slice, on the current stream and on a
+    side stream) write bitwise what the plain slice calls write, and the
+    slices of both ops compose to the oracle's full results."""
+    num = 4
+    ws = inputs.random_sum(dtype, 3, 70001, 1450)
+    wf = inputs.random_fused(dtype, 4, 37, 2048, 1460)
+    sp = [dev(p, dtype) for p in ws.partials]
+    fp = [dev(p, dtype) for p in wf.partials]
+    weight, bias, res = dev(wf.weight, dtype), dev(wf.bias, dtype), dev(wf.residual, dtype)
+    s_out = Guarded(ws.n, dtype)
+    f_out, f_inter = Guarded(wf.n, dtype), Guarded(wf.n, dtype)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for k in range(num):
+        cs = ar.prepare_sum_slice(sp, s_out.t, k, num)
+        cf = ar.prepare_residual_rmsnorm_slice(fp, weight, wf.eps, f_out.t, f_inter.t, k, num, bias=bias,
+                                               residual=res)
+        if k % 2:
+            cs(side)
+            cf(side)
+        else:
+            cs()
+            cf()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for g in (s_out, f_out, f_inter):
+        g.check_guards()
+    assert_bitexact(host_bits(s_out.t), bits(oracle_sum(ws)), dtype, "prepared sum slices")
+    ref_out, ref_inter = oracle_fused(wf)
+    assert_bitexact(host_bits(f_inter.t), ref_inter, dtype, "prepared fused slices intermediate")
+    assert_output_close(host_bits(f_out.t), ref_out, dtype, "prepared fused slices output")
+    p_out, p_inter = torch.empty_like(fp[0]), torch.empty_like(fp[0])
+    for k in range(num):
+        ar.ar_residual_rmsnorm_slice(fp, weight, wf.eps, p_out, p_inter, k, num, bias=bias, residual=res)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(f_out.t), host_bits(p_out)) and np.array_equal(host_bits(f_inter.t),
+                                                                                     host_bits(p_inter))
+    with pytest.raises(ar.ArError, match="AR_ERR_SLICE"):
+        ar.prepare_sum_slice(sp, s_out.t, num, num)()
+
+
 def test_two_shot_split_at_the_large_shapes():
     """Eight slices of the large fused workload and four of the large sum
     compose to the oracle's full results."""
