@@ -54,6 +54,12 @@
  * never throws. On a validation error nothing is launched and no output is
  * touched. Validation makes no HIP call, so it works on a host without a GPU.
  *
+ * Diagnostics: with the environment variable AR_LOG set to anything but
+ * "0" when the library is first used (it is read once per process), every
+ * launch prints its dispatch decision to stderr - kernel, rank count, shape,
+ * grid and workgroup size - and a failed launch prints the HIP error text.
+ * Validation errors print nothing; they are returned as status codes.
+ *
  * Size bound: elts_total * sizeof(T) must fit in size_t, and every buffer's
  * byte range [ptr, ptr + bytes) (full-size buffers: elts_total elements;
  * bias and weight: hidden_size elements) must end inside the address space.

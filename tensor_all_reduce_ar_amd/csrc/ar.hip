@@ -884,6 +884,10 @@ void launch_fused_pack_as(const FusedArgs &a, unsigned grid, int threads, int de
     const bool dispatched = MODE != kPlain && R >= 3 && R <= 5 && a.ppr <= 1024;
     if (grid > resident && !dispatched)
         grid = static_cast<unsigned>(resident);
+    if (log_enabled())
+        fprintf(stderr, "[ar] fused pack R=%d rows=%zu H=%d ppr=%d ppt=%d block=%d bound=%d walk=%s grid=%u (%s)\n", R,
+                a.rows, a.hidden, a.ppr, PPT, threads, BOUND, MODE == kFull ? "full" : MODE == kRagged ? "ragged" : "plain",
+                grid, grid < a.rows ? "resident, looping over rows" : "one workgroup per row");
     hipLaunchKernelGGL((ar_rmsnorm_pack_kernel<E, R, PPT, BOUND, MODE>), dim3(grid), dim3(threads), 0, stream, a);
 }
 
@@ -1031,9 +1035,6 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
                     a.ppr, kWideThreads, grid);
         hipLaunchKernelGGL((ar_rmsnorm_wide_kernel<E, R>), dim3(grid), dim3(kWideThreads), 0, stream, a);
     } else if (vec) {
-        if (log_enabled())
-            fprintf(stderr, "[ar] fused pack R=%d rows=%zu H=%d ppr=%d ppt=%d block=%d bound=%d grid=%u\n", R,
-                    a.rows, a.hidden, a.ppr, g.ppt, g.threads, g.bound, grid);
         const int t = g.threads;
         bool ok = false;
         if (g.bound == kFusedMaxThreads) {
