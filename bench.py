@@ -667,7 +667,7 @@ def main():
             "bytes_per_step": f["bytes"], "rotating_input_sets": f["nsets"], "seeds": w.seeds,
             "partials": ("one allocation per set from allocate_workspace (ar_partials_layout's staggered slots)"
                          if head_layout == "slab" else "one torch allocation per partial"),
-            "distribution": "normal(mean, variance): partials N(0,1/R), residual N(0,1), weight N(1,0.1)",
+            "distribution": w.distribution,
         },
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {
