@@ -106,18 +106,30 @@ def rotation_sets(bytes_per_set: int, out_bytes_per_set: int) -> int:
     return max(2, -(-4 * LLC_BYTES // bytes_per_set), -(-2 * LLC_BYTES // out_bytes_per_set))
 
 
+LEAD_IN_MAX = 8  # untimed launches queued right before a timed region
+
+
 def time_launches(torch, launch, nsets, steps, warmup, stream):
     """Whole-region timing (ms per step over `steps` back-to-back launches) and
     per-launch timing (a list of `steps` kernel durations in ms, each between
-    two events around one launch), both with HIP events on the launch stream."""
+    two events around one launch), both with HIP events on the launch stream.
+    After the warmup, a lead-in of untimed launches (one rotation cycle, at
+    most LEAD_IN_MAX) is queued just before the start event, so that the
+    device is already busy and the host well ahead when the region starts: a
+    host pause early in the region then finds kernels queued instead of an
+    idle device. The start event fires when the lead-in has finished, so the
+    region holds exactly the `steps` timed launches."""
     for i in range(warmup):
         launch(i % nsets)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    lead = min(nsets, LEAD_IN_MAX)
     gc_was_on = gc.isenabled()
     gc.disable()  # no collector pause while the host queues a timed region
     try:
+        for i in range(lead):
+            launch((nsets - lead + i) % nsets)
         start.record(stream)
         for i in range(steps):
             launch(i % nsets)

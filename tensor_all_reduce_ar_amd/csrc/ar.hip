@@ -513,17 +513,27 @@ __global__ __launch_bounds__(BOUND) void ar_rmsnorm_pack_kernel(FusedArgs a)
 #pragma unroll
             for (int p = 0; p < PPT; ++p) {
                 const int j = threadIdx.x + p * T;
+                // The wait counter is in order: a bias load issued after the
+                // next slot's loads makes this slot's sums wait for those too.
+                // Issuing it first was measured faster (8-rank rows with bias:
+                // 3.5 % at 4 x 256, 1.3-1.9 % on 512 lanes) except at 5..8
+                // packs on the 256-lane bound (0.8-1.7 % slower), which keep
+                // it after.
+                constexpr bool kBiasFirst = !(BOUND == 256 && PPT >= 5);
+                u32x4 bq = {0, 0, 0, 0};
+                if constexpr (kHoist)
+                    bq = bh[p];
+                else if (kBiasFirst && bias && (p + 1 < PPT || last_ok))
+                    bq = bias[j];
                 if (p + 2 < PPT || (p + 1 < PPT && last_ok))
                     load_slot<R>(a, row0 + j + T, v[(p + 1) & 1], rq[(p + 1) & 1]);
                 if (p + 1 < PPT || last_ok) {
-                    u32x4 bq;
-                    if constexpr (kHoist) {
-                        bq = bh[p];
-                        w[p] = wh[p];
-                    } else {
+                    if constexpr (!kHoist && !kBiasFirst)
                         bq = bias ? bias[j] : u32x4{0, 0, 0, 0};
+                    if constexpr (kHoist)
+                        w[p] = wh[p];
+                    else
                         w[p] = weight[j];
-                    }
                     sp[p] = fused_pre_norm<E, R>(v[p & 1], bias != nullptr, bq, a.residual != nullptr, rq[p & 1]);
                     ss += sum_squares<E>(sp[p]);
                 }
@@ -590,9 +600,9 @@ __global__ __launch_bounds__(W * kWave) void ar_rmsnorm_wave_kernel(FusedArgs a)
 #pragma unroll
         for (int p = 0; p < SL; ++p) {
             const int j = lane + p * kWave;
+            const u32x4 bq = bias ? bias[j] : u32x4{0, 0, 0, 0};  // before the next slot's loads (in-order waits)
             if (p + 1 < SL)
                 load_slot<R>(a, row0 + j + kWave, v[(p + 1) & 1], rq[(p + 1) & 1]);
-            const u32x4 bq = bias ? bias[j] : u32x4{0, 0, 0, 0};
             sp[p] = fused_pre_norm<E, R>(v[p & 1], bias != nullptr, bq, a.residual != nullptr, rq[p & 1]);
             ss += sum_squares<E>(sp[p]);
             asm volatile("" ::: "memory");
