@@ -1130,8 +1130,6 @@ struct FusedLauncher {
     }
 };
 
-
-
 // The sum on already-validated params (any elts_total > 0).
 int32_t run_sum(const ar_params_t *p, hipStream_t stream)
 {
