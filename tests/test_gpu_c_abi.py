@@ -1,8 +1,10 @@
 """The C ABI from plain C: tests/c_abi_check.c (built by tests/c_abi_build.py,
 which build() runs) drives libar.so with HIP runtime memory and a stream of
-its own, and checks a sum, two fused calls and rejected calls against the
-CPU oracle. It runs as a child process with a time limit."""
+its own, and checks against the CPU oracle a sum, two fused calls, rejected
+calls, the two-shot slices of both ops, the unfused path and a sum replayed
+from a HIP graph. It runs as a child process with a time limit."""
 import os
+import re
 import subprocess
 
 import pytest
@@ -33,7 +35,18 @@ def test_dispatch_log():
     res = subprocess.run([EXE], capture_output=True, text=True, timeout=120, env=env)
     assert res.returncode == 0 and "c_abi_check: OK" in res.stdout, res.stdout + res.stderr
     log = [line for line in res.stderr.splitlines() if line.startswith("[ar] ")]
-    assert any(line.startswith("[ar] sum pack R=3 V=8 n=10007 ") for line in log), log
-    assert any(line.startswith("[ar] fused pack R=4 rows=37 H=640 ppr=80 ") for line in log), log
-    assert any(line.startswith("[ar] fused pack R=2 rows=9 H=1024 ppr=256 ") for line in log), log
-    assert len(log) == 3, log
+
+    def count(prefix):
+        return sum(line.startswith(prefix) for line in log)
+
+    for prefix in ("[ar] sum pack R=3 V=8 n=10007 ", "[ar] fused pack R=4 rows=37 H=640 ppr=80 ",
+                   "[ar] fused pack R=2 rows=9 H=1024 ppr=256 ", "[ar] sum pack R=8 V=8 n=65536 ",
+                   "[ar] fused pack R=1 rows=16 H=4096 ppr=512 ", "[ar] sum pack R=2 V=8 n=1000003 "):
+        assert count(prefix) == 1, (prefix, log)
+    # the slices: 3 sums that share 10007 elements, 4 fused calls that share 37 rows
+    sliced = [int(m.group(1)) for m in (re.match(r"\[ar\] sum pack R=4 V=8 n=(\d+) ", x) for x in log) if m]
+    assert sorted(sliced) == [3335, 3336, 3336], log
+    rows = [int(m.group(1)) for m in (re.match(r"\[ar\] fused pack R=3 rows=(\d+) H=1536 ", x) for x in log) if m]
+    assert sorted(rows) == [7, 10, 10, 10], log
+    # one line per launched call; the graph's replays launch from the graph, not through the library
+    assert len(log) == 13, log
