@@ -943,12 +943,14 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
     }
 }
 
-// Rows of 2049..4096 packs in 16-bit types: 512 lanes x PPT (5..8) packs in the
-// pipelined variant, full or ragged (one workgroup per CU: up to 221 VGPRs).
-// Against the two-pass wide kernel this measured 15-18 % faster on hidden
-// 18432..32768 (bf16, 8 ranks) and 2.4 % on fp16 2-rank rows of 32768. Only
-// these two forms are instantiated at this bound; fp32 rows of this width
-// keep the wide kernel (its instances here would spill).
+// Rows of 2049..4096 packs in 16-bit types, and in fp32 with one or two
+// ranks: 512 lanes x PPT (5..8) packs in the pipelined variant, full or ragged
+// (one workgroup per CU: up to 230 VGPRs). Against the two-pass wide kernel
+// this measured 15-18 % faster on hidden 18432..32768 (bf16, 8 ranks), 2.4 %
+// on fp16 2-rank rows of 32768, and 5-30 % on fp32 one- and two-rank rows of
+// 9216..16384. Only these two forms are instantiated at this bound; fp32
+// rows of this width with more ranks keep the wide kernel (some of their
+// instances here would spill).
 // Returns false, launching nothing, unless the row needs exactly PPT slots of
 // kWideRowLanes lanes.
 template <class E, int R, int PPT>
@@ -1017,7 +1019,8 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
         a.ppr = static_cast<int>(static_cast<size_t>(f.hidden_size) * E::kSize / kPackBytes);
         dev = current_device();
         cus = device_cus(dev);
-        g = ar_geometry::fused_geometry(a.ppr, ar_geometry::latency_layout(a.ppr, a.rows, cus), E::kSize == 2);
+        g = ar_geometry::fused_geometry(a.ppr, ar_geometry::latency_layout(a.ppr, a.rows, cus),
+                                        ar_geometry::wide_rows_in_registers(E::kSize, R));
     }
     if (vec && g.waves > 0) {
         if (log_enabled())
@@ -1054,7 +1057,7 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
             default: break;
             }
         } else if (g.bound == kWideRowLanes && g.ppt > 2) {
-            if constexpr (E::kSize == 2) {
+            if constexpr (ar_geometry::wide_rows_in_registers(E::kSize, R)) {
                 switch (g.ppt) {
                 case 5: ok = launch_fused_pack_wide<E, R, 5>(a, grid, t, dev, cus, stream); break;
                 case 6: ok = launch_fused_pack_wide<E, R, 6>(a, grid, t, dev, cus, stream); break;

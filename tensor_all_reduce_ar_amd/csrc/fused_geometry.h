@@ -18,7 +18,8 @@ constexpr int kWave = 64;
 // lanes, which keeps every variant within the VGPR budget of its launch bound
 // (those on 256 lanes run pipelined, the last slot possibly partial, and so
 // do rows of exactly 1024 packs, as 4 x 256); rows of 2049..4096 packs in
-// 16-bit types take 5..8 pipelined packs per lane on 512 lanes;
+// 16-bit types, and in fp32 with one or two ranks, take 5..8 pipelined packs
+// per lane on 512 lanes;
 // rows of 320, 384 and 640 packs take 64 or 128 lanes (see fused_geometry).
 // Latency layout (no more rows than CUs - for rows of 1024..2048 packs, no
 // more than three quarters of them - and rows of 513..2048 packs): up to 1024
@@ -32,6 +33,17 @@ constexpr int kFullLanes = 256;     // pipelined variant: workgroup size, at mos
 constexpr int kRowsMaxPacks = 512;  // multi-row kernel: widest row, and workgroup size bound
 constexpr int kWideRowLanes = 512;  // register path for rows of 2049..4096 packs (16-bit types)
 constexpr int kWideThreads = 1024;  // workgroup size of the two-pass kernel for rows wider than that
+
+// Whether rows of 2049..4096 packs take the 512-lane register path: always in
+// 16-bit types, and in fp32 with up to kFp32WideRowMaxRanks ranks, whose
+// instances keep every value in registers at 5..8 packs per lane (101-230
+// VGPRs); from 3 ranks up some fp32 instances there spill, so those rows take
+// the two-pass wide kernel.
+constexpr int kFp32WideRowMaxRanks = 2;
+constexpr bool wide_rows_in_registers(int elem_size, int ranks)
+{
+    return elem_size == 2 || ranks <= kFp32WideRowMaxRanks;
+}
 
 // How the one-row-per-workgroup kernel walks a lane's slots.
 enum PipelineMode {
@@ -68,11 +80,13 @@ struct FusedGeometry {
 // (6 waves of 2 packs) gained at most 2 % and rows of 896 (7 waves) lost on
 // 128 lanes, so they keep the default. Rows of 1025..2048 packs fill 5..8
 // slots on 256 lanes, all full or all but the last, and so run pipelined too.
-// Rows of 2049..4096 packs in 16-bit types (`wide_rows_in_registers`) take
-// 512 lanes x ceil(ppr / 512) packs, pipelined, at any row count (replayed
-// from a HIP graph, 5-36 % faster than the two-pass kernel at 16..256 rows of
-// hidden 20480 and 32768); wider rows, and fp32 rows past 2048 packs, take
-// the two-pass wide kernel.
+// Rows of 2049..4096 packs where `wide_rows_in_registers` holds (16-bit
+// types; fp32 with one or two ranks) take 512 lanes x ceil(ppr / 512) packs,
+// pipelined, at any row count (replayed from a HIP graph, 5-36 % faster than
+// the two-pass kernel at 16..256 rows of hidden 20480 and 32768 in 16-bit
+// types; 5-30 % on fp32 one- and two-rank rows of hidden 9216..16384); wider
+// rows, and the other fp32 rows past 2048 packs, take the two-pass wide
+// kernel.
 // Latency layout (`few_rows`, rows of more than 512 packs): ceil(ppr / 1024)
 // packs per lane, up to kLatencyMaxPPT.
 inline FusedGeometry fused_geometry(int ppr, bool few_rows, bool wide_rows_in_registers)

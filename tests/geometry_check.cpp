@@ -1,7 +1,8 @@
 // Host check of the fused op's launch geometry (csrc/fused_geometry.h) for
 // every row width of 1..8192 packs, both layouts (few rows or many) and both
-// element-size classes (16-bit types take the 512-lane register path for rows
-// of 2049..4096 packs, fp32 does not). For each shape it checks what the
+// classes of element type and rank count (16-bit types, and fp32 with one or
+// two ranks, take the 512-lane register path for rows of 2049..4096 packs;
+// fp32 with more ranks does not). For each shape it checks what the
 // kernels assume: whole waves, no more lanes than the instance's launch
 // bound, lanes x packs covering the row, no lane slot that is empty for every
 // lane, a (packs per lane, launch bound, slot walk) combination that the
@@ -120,6 +121,13 @@ int main()
                 if (mode != kPlain && (ppt < 3 || (threads > kFullLanes && threads != kWideRowLanes)))
                     fail("pipeline_mode: pipelined walk outside the compiled shapes", ppr, false, false, none);
             }
+    // Which element types and rank counts take the 512-lane register path.
+    for (int ranks = 1; ranks <= 8; ++ranks) {
+        if (!wide_rows_in_registers(2, ranks))
+            fail("16-bit rows kept off the 512-lane register path", ranks, false, false, none);
+        if (wide_rows_in_registers(4, ranks) != (ranks <= kFp32WideRowMaxRanks))
+            fail("fp32 rank rule of the 512-lane register path", ranks, false, true, none);
+    }
     if (failures) {
         std::printf("%d failures\n", failures);
         return 1;

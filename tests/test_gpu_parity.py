@@ -225,9 +225,9 @@ def test_sum_deterministic_and_on_a_side_stream():
 def test_fused_widths(dtype, hidden):
     """Few rows: the register-row kernel in its latency layout (one pack per
     lane up to 1024 packs a row, two up to 2048), the 512-lane register path
-    for 16-bit rows of 2049..4096 packs, the wide two-pass vector kernel past
-    that (and past 2048 packs in fp32), and the element kernel for rows whose
-    byte size is not a multiple of 16 (4100 fp16/bf16)."""
+    for rows of 2049..4096 packs (16-bit types, and fp32 at these two ranks),
+    the wide two-pass vector kernel past that, and the element kernel for rows
+    whose byte size is not a multiple of 16 (4100 fp16/bf16)."""
     for rows in (1, 7, 33, 64):
         if rows * hidden > 1 << 21:
             continue
@@ -253,8 +253,8 @@ def test_fused_widths_at_the_layout_switch(dtype, hidden):
     1025..2047 packs, 512 lanes with 5..8 packs (full or ragged) for rows of
     2049..4096 packs in 16-bit types, up to 512 lanes with 1..8 packs per
     lane for the rest, and the two-pass wide kernel past that (fp32 rows of
-    more than 2048 packs, 16-bit rows of more than 4096). The row count at the
-    switch and one past it."""
+    more than 2048 packs at the 8 ranks used here, 16-bit rows of more than
+    4096). The row count at the switch and one past it."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for rows in (cus, cus + 1):
         note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
@@ -276,6 +276,30 @@ def test_fused_rows_at_the_latency_switch(dtype, hidden):
         w = inputs.random_fused(dtype, 8, rows, hidden, 380 + rows % 5)
         got_out, got_inter = run_fused(w)
         check_fused(w, got_out, got_inter)
+
+
+@pytest.mark.parametrize("ranks", [1, 2, 3])
+@pytest.mark.parametrize("hidden", [8196, 8200, 9216, 10240, 12288, 14336, 16376, 16384])
+def test_fp32_rows_of_2049_to_4096_packs(ranks, hidden):
+    """fp32 rows of 2049..4096 packs: with one or two ranks the 512-lane
+    register path (5..8 packs per lane, full, or ragged down to one lane in
+    the last slot at 8196), with three the two-pass wide kernel; a few rows
+    and more rows than CUs, then the same call with the intermediate written
+    over the residual and the output over the last partial."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for rows in (3, cus + 1):
+        note(f"[parity] fused fp32 R={ranks} H={hidden} rows={rows}")
+        w = inputs.random_fused("fp32", ranks, rows, hidden, 730 + rows % 7 + ranks)
+        got_out, got_inter = run_fused(w)
+        check_fused(w, got_out, got_inter)
+    ref_out, ref_inter = ref_fused(w)
+    parts = [dev(p, "fp32") for p in w.partials]
+    res = dev(w.residual, "fp32")
+    ar.ar_residual_rmsnorm(parts, dev(w.weight, "fp32"), w.eps, parts[-1], res, bias=dev(w.bias, "fp32"),
+                           residual=res)
+    torch.cuda.synchronize()
+    assert_bitexact(host_bits(res), ref_inter, "fp32", "intermediate in place of the residual")
+    assert_output_close(host_bits(parts[-1]), ref_out, "fp32", "output in place of the last partial")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
