@@ -61,6 +61,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kPackBytes = 16;
 using ar_geometry::FusedGeometry;
 using ar_geometry::kFull;
+using ar_geometry::kChunkLanes;
+using ar_geometry::kChunkPacks;
 using ar_geometry::kFusedMaxThreads;
 using ar_geometry::kMaxPPT;
 using ar_geometry::kPlain;
@@ -720,6 +722,109 @@ __global__ __launch_bounds__(kWideThreads) void ar_rmsnorm_wide_kernel(FusedArgs
     }
 }
 
+// Rows of more than 4096 packs when there are few of them (no more than half
+// the CUs): one workgroup per chunk of kChunkPacks packs of a row
+// (kChunkLanes lanes x 2 packs, all loads in flight), over three launches.
+// The chunks' sums of squares pass between the launches through the head
+// word (the first 4 bytes) of each chunk's region of `out`, which only the
+// last launch overwrites, and only from the workgroup that reads it - so the
+// library still needs no scratch memory. Chunk c of a row covers packs
+// c * kChunkPacks .. of that row.
+__device__ __forceinline__ float *chunk_head(const FusedArgs &a, size_t row0, int c)
+{
+    return reinterpret_cast<float *>(static_cast<u32x4 *>(a.out) + row0 + static_cast<size_t>(c) * kChunkPacks);
+}
+
+// Launch 1: S for the chunk (stored with normal stores, so launch 3 finds it in
+// cache), and the chunk's sum of squares in its head word.
+template <class E, int R>
+__global__ __launch_bounds__(kChunkLanes) void ar_rmsnorm_chunk_sum_kernel(FusedArgs a, int chunks)
+{
+    constexpr int U = kChunkPacks / kChunkLanes;
+    __shared__ float part[kChunkLanes / kWave];
+    const u32x4 *bias = static_cast<const u32x4 *>(a.bias);
+    const size_t units = a.rows * static_cast<size_t>(chunks);
+    for (size_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const size_t row = u / static_cast<size_t>(chunks);
+        const int c = static_cast<int>(u - row * static_cast<size_t>(chunks));
+        const size_t row0 = row * static_cast<size_t>(a.ppr);
+        const int j0 = c * kChunkPacks + static_cast<int>(threadIdx.x);
+        u32x4 v[U][R], rq[U], bq[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int j = j0 + k * kChunkLanes;
+            if (j < a.ppr) {
+                load_slot<R>(a, row0 + j, v[k], rq[k]);
+                bq[k] = bias ? bias[j] : u32x4{0, 0, 0, 0};
+            }
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int j = j0 + k * kChunkLanes;
+            if (j < a.ppr) {
+                const u32x4 sp = fused_pre_norm<E, R>(v[k], bias != nullptr, bq[k], a.residual != nullptr, rq[k]);
+                static_cast<u32x4 *>(a.inter)[row0 + j] = sp;
+                ss += sum_squares<E>(sp);
+            }
+        }
+        const float t = block_sum(ss, part);
+        if (threadIdx.x == 0)
+            *chunk_head(a, row0, c) = t;
+        __syncthreads();  // `part` is rewritten by the next chunk
+    }
+}
+
+// Launch 2: one lane per row adds its chunks' sums of squares in chunk order
+// and writes the row's rstd into every chunk's head word.
+__global__ __launch_bounds__(kWave) void ar_rmsnorm_row_scale_kernel(FusedArgs a, int chunks)
+{
+    const size_t stride = static_cast<size_t>(gridDim.x) * kWave;
+    for (size_t row = static_cast<size_t>(blockIdx.x) * kWave + threadIdx.x; row < a.rows; row += stride) {
+        const size_t row0 = row * static_cast<size_t>(a.ppr);
+        float ss = *chunk_head(a, row0, 0);
+        for (int c = 1; c < chunks; ++c)
+            ss = ss + *chunk_head(a, row0, c);
+        const float rstd = rms_scale(ss, a.hidden, a.eps);
+        for (int c = 0; c < chunks; ++c)
+            *chunk_head(a, row0, c) = rstd;
+    }
+}
+
+// Launch 3: the chunk's rstd from its head word, then (after a barrier: the
+// head is also the chunk's first output pack) the normed output from S.
+template <class E>
+__global__ __launch_bounds__(kChunkLanes) void ar_rmsnorm_chunk_norm_kernel(FusedArgs a, int chunks)
+{
+    constexpr int U = kChunkPacks / kChunkLanes;
+    const u32x4 *weight = static_cast<const u32x4 *>(a.weight);
+    const size_t units = a.rows * static_cast<size_t>(chunks);
+    for (size_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const size_t row = u / static_cast<size_t>(chunks);
+        const int c = static_cast<int>(u - row * static_cast<size_t>(chunks));
+        const size_t row0 = row * static_cast<size_t>(a.ppr);
+        const int j0 = c * kChunkPacks + static_cast<int>(threadIdx.x);
+        float rstd = *chunk_head(a, row0, c);
+        asm volatile("" : "+v"(rstd));  // the load has returned before the barrier below
+        u32x4 sq[U], wq[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int j = j0 + k * kChunkLanes;
+            if (j < a.ppr) {
+                sq[k] = static_cast<const u32x4 *>(a.inter)[row0 + j];
+                wq[k] = weight[j];
+            }
+        }
+        __syncthreads();  // every lane holds rstd before lane 0 overwrites the head
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int j = j0 + k * kChunkLanes;
+            if (j < a.ppr)
+                st16(static_cast<u32x4 *>(a.out) + row0 + j, normed_pack<E>(sq[k], rstd, wq[k]));
+        }
+    }
+}
+
 // Fused op, element-wise, one row per workgroup: pass 1 forms, stores and
 // squares S; pass 2 re-reads the S this lane stored and writes the norm.
 template <class E, int R>
@@ -1042,6 +1147,16 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
             ok = launch_fused_rows<E, R, 2>(a, g.threads, dev, cus, stream);
         if (!ok)
             return AR_ERR_SHAPE;  // unreachable: fused_geometry only yields shapes the kernel takes
+    } else if (vec && g.ppt == 0 && ar_geometry::wide_rows_chunked(a.ppr, a.rows, cus)) {
+        const int chunks = (a.ppr + kChunkPacks - 1) / kChunkPacks;
+        const unsigned cgrid = clamp_grid(a.rows * static_cast<size_t>(chunks));
+        const unsigned sgrid = clamp_grid((a.rows + kWave - 1) / kWave);
+        if (log_enabled())
+            fprintf(stderr, "[ar] fused chunked R=%d rows=%zu H=%d ppr=%d chunks/row=%d block=%d grid=%u\n", R, a.rows,
+                    a.hidden, a.ppr, chunks, kChunkLanes, cgrid);
+        hipLaunchKernelGGL((ar_rmsnorm_chunk_sum_kernel<E, R>), dim3(cgrid), dim3(kChunkLanes), 0, stream, a, chunks);
+        hipLaunchKernelGGL(ar_rmsnorm_row_scale_kernel, dim3(sgrid), dim3(kWave), 0, stream, a, chunks);
+        hipLaunchKernelGGL((ar_rmsnorm_chunk_norm_kernel<E>), dim3(cgrid), dim3(kChunkLanes), 0, stream, a, chunks);
     } else if (vec && g.ppt == 0) {
         if (log_enabled())
             fprintf(stderr, "[ar] fused wide R=%d rows=%zu H=%d ppr=%d block=%d grid=%u\n", R, a.rows, a.hidden,

@@ -302,6 +302,82 @@ def test_fp32_rows_of_2049_to_4096_packs(ranks, hidden):
     assert_output_close(host_bits(parts[-1]), ref_out, "fp32", "output in place of the last partial")
 
 
+CHUNKED_CASES = [("bf16", 8, 32776), ("fp16", 2, 65536), ("bf16", 3, 131072), ("fp16", 1, 40968),
+                 ("fp32", 8, 16388), ("fp32", 2, 32768), ("fp32", 3, 20488), ("fp32", 6, 16392)]
+
+
+@pytest.mark.parametrize("dtype,ranks,hidden", CHUNKED_CASES)
+def test_fused_wide_rows_chunked(dtype, ranks, hidden):
+    """Rows of more than 4096 packs, at no more rows than half the CUs: one
+    workgroup per chunk of 1024 packs over three launches, the chunks' sums of
+    squares passed through the head words of the output. Widths with a short
+    last chunk (4097, 4098, 5121 and 5122 packs) and 8 and 16 whole chunks,
+    in every type. Row counts 1, 7 and half the CUs (chunked), and one more
+    (the two-pass kernel)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for rows in (1, 7, cus // 2, cus // 2 + 1):
+        if rows * hidden > 12 << 20:
+            continue
+        note(f"[parity] fused chunked {dtype} R={ranks} H={hidden} rows={rows} (CUs {cus})")
+        w = inputs.random_fused(dtype, ranks, rows, hidden, 760 + rows % 11 + ranks)
+        got_out, got_inter = run_fused(w)
+        check_fused(w, got_out, got_inter)
+
+
+def test_fused_wide_rows_chunked_aliasing_and_repeat():
+    """The chunked path with the output written over a partial (whose head
+    words then carry the sums of squares between the launches) and the
+    intermediate over the residual; then two plain calls, bitwise equal."""
+    for dtype, ranks, rows, hidden in (("bf16", 4, 9, 65536), ("fp32", 3, 5, 16392)):
+        note(f"[parity] fused chunked aliasing {dtype} R={ranks} H={hidden} rows={rows}")
+        w = inputs.random_fused(dtype, ranks, rows, hidden, 790)
+        ref_out, ref_inter = ref_fused(w)
+        parts = [dev(p, dtype) for p in w.partials]
+        res = dev(w.residual, dtype)
+        ar.ar_residual_rmsnorm(parts, dev(w.weight, dtype), w.eps, parts[1], res, bias=dev(w.bias, dtype),
+                               residual=res)
+        torch.cuda.synchronize()
+        assert_bitexact(host_bits(res), ref_inter, dtype, "intermediate in place of the residual")
+        assert_output_close(host_bits(parts[1]), ref_out, dtype, "output in place of partial 1")
+        a, b = run_fused(w), run_fused(w)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), "repeat calls differ"
+
+
+def test_fused_wide_rows_chunked_from_a_graph():
+    """A chunked call (three launches) captured into a HIP graph and replayed
+    three times, outputs filled with NaN before each replay and new partials
+    copied in before the last: every replay matches the oracle."""
+    note("[parity] fused chunked graph replay")
+    ws = [inputs.random_fused("bf16", 8, 6, 65536, 800 + k) for k in range(2)]
+    parts = [dev(p, "bf16") for p in ws[0].partials]
+    wt, b, q = dev(ws[0].weight, "bf16"), dev(ws[0].bias, "bf16"), dev(ws[0].residual, "bf16")
+    out, inter = torch.empty_like(parts[0]), torch.empty_like(parts[0])
+    call = ar.prepare_residual_rmsnorm(parts, wt, ws[0].eps, out, inter, bias=b, residual=q)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        k = 1 if rep == 2 else 0
+        if rep == 2:
+            for t, p in zip(parts, ws[1].partials):
+                t.copy_(dev(p, "bf16"))
+        out.fill_(float("nan"))
+        inter.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        w = inputs.Workload("graph-chunked", "fused", "bf16", 8, ws[k].n, ws[k].hidden, ws[k].partials,
+                            ws[0].bias, ws[0].residual, ws[0].weight, ws[0].eps)
+        check_fused(w, host_bits(out), host_bits(inter))
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("ranks", range(1, 9))
 def test_fused_ranks(dtype, ranks):
