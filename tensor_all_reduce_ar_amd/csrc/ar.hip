@@ -32,7 +32,11 @@
 //  * the workgroup shape follows the row width: whole power-of-two numbers of
 //    waves per workgroup where the width allows (the four SIMDs of a CU get
 //    equal shares), more lanes per row when there are too few rows to fill
-//    the chip.
+//    the chip;
+//  * rows wider than the register budget store S and read it back: one
+//    workgroup per row in two passes, or, when there are few such rows, one
+//    workgroup per 1024-pack chunk over three launches, the chunks' sums of
+//    squares passed through words of the output that are overwritten last.
 // Shapes the vector path does not cover (pointers not 16-byte aligned, rows
 // whose byte size is not a multiple of 16, rows wider than the register
 // budget) run element-wise kernels with the same arithmetic.
