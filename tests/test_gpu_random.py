@@ -6,7 +6,8 @@ sum), whether bias and residual are present, an aliasing mode the ABI allows
 offsets that move pointers off 16-byte alignment, and is compared with the
 oracle on the same inputs: sums and pre-norm sums bit for bit, normed outputs
 within 1e-5 relative (fp32) or 2 ulp (fp16/bf16). Outputs that are not aliased
-to an input carry canaries on both sides.
+to an input carry canaries on both sides. A second set draws fused cases with
+rows wider than 2048 packs (the 512-lane, two-pass and chunked paths).
 """
 import numpy as np
 import pytest
@@ -22,6 +23,8 @@ from gpu_util import TORCH_DT, Guarded, assert_bitexact, assert_output_close, bi
 DTYPES = ("fp32", "fp16", "bf16")
 CASES = 600
 MAX_ELEMS = 1 << 21
+WIDE_CASES = 150
+WIDE_MAX_ELEMS = 1 << 23
 
 
 def draw(case):
@@ -56,12 +59,47 @@ def device_with_offset(a, dtype, off):
     return t[off:]
 
 
+def draw_wide(case):
+    """A fused case with rows of 2049..9000 16-byte packs - the 512-lane
+    register path (fp32 up to 2 ranks, 16-bit types up to 4096 packs), the
+    two-pass kernel, and the chunked path (more than 4096 packs, no more rows
+    than half the CUs) - at 1..WIDE_MAX_ELEMS elements."""
+    rng = np.random.Generator(np.random.PCG64(50_000 + case))
+    c = {"op": "fused", "dtype": DTYPES[rng.integers(3)], "ranks": int(rng.integers(1, 9)), "seed": 60_000 + case}
+    v = 4 if c["dtype"] == "fp32" else 8
+    hidden = int(rng.integers(2049, 9001)) * v
+    top = WIDE_MAX_ELEMS // hidden
+    rows = int(rng.choice([1, 2, int(rng.integers(1, 129)), int(rng.integers(1, top + 1))]))
+    rows = max(1, min(rows, top))
+    c.update(hidden=hidden, rows=rows, n=hidden * rows, bias=bool(rng.random() < 0.5),
+             residual=bool(rng.random() < 0.7))
+    modes = ["none", "out=partial", "inter=partial"] + (["inter=residual"] if c["residual"] else [])
+    c["alias"] = modes[rng.integers(len(modes))]
+    c["alias_rank"] = int(rng.integers(c["ranks"]))
+    c["offsets"] = [0] * (c["ranks"] + 2)
+    return c
+
+
 @pytest.mark.gpu
 @pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
 @pytest.mark.parametrize("case", range(CASES))
 def test_random_case_matches_oracle(case):
     c = draw(case)
     note(f"[random] case {case}: {c}")
+    run_case(c, f"random case {case}")
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+@pytest.mark.parametrize("case", range(WIDE_CASES))
+def test_random_wide_row_case_matches_oracle(case):
+    c = draw_wide(case)
+    note(f"[random] wide case {case}: {c}")
+    run_case(c, f"random wide case {case}")
+
+
+def run_case(c, label):
+    """Runs one drawn case on the GPU and compares it with the oracle."""
     dt, R = c["dtype"], c["ranks"]
     if c["op"] == "sum":
         w = inputs.random_sum(dt, R, c["n"], c["seed"])
@@ -83,7 +121,7 @@ def test_random_case_matches_oracle(case):
             g.check_guards()
         ref = empty_host(w.n, dt)
         oracle.ar_sum(dt, w.partials, ref)
-        assert_bitexact(host_bits(out), bits(ref), dt, f"random sum case {case}")
+        assert_bitexact(host_bits(out), bits(ref), dt, f"{label}: sum")
         return
 
     residual = device_with_offset(w.residual, dt, c["offsets"][R + 1]) if w.residual is not None else None
@@ -104,8 +142,8 @@ def test_random_case_matches_oracle(case):
     ref_out, ref_inter = empty_host(w.n, dt), empty_host(w.n, dt)
     oracle.ar_residual_rmsnorm(dt, w.partials, w.hidden, w.weight, w.eps, ref_out, ref_inter, bias=w.bias,
                                residual=w.residual)
-    assert_bitexact(host_bits(inter), bits(ref_inter), dt, f"random fused case {case}: intermediate")
-    assert_output_close(host_bits(out), bits(ref_out), dt, f"random fused case {case}: output")
+    assert_bitexact(host_bits(inter), bits(ref_inter), dt, f"{label}: intermediate")
+    assert_output_close(host_bits(out), bits(ref_out), dt, f"{label}: output")
 
 
 def test_random_cases_cover_every_dimension():
@@ -123,3 +161,18 @@ def test_random_cases_cover_every_dimension():
     assert any(c["hidden"] * (4 if c["dtype"] == "fp32" else 2) % 16 for c in fused)
     assert any(c["rows"] == 1 for c in fused)
     assert any(c["alias"] == "out=partial" for c in cs if c["op"] == "sum")
+
+
+def test_random_wide_cases_cover_every_path():
+    """Host only. The wide-row draw reaches every type and rank count, rows
+    of 2049..4096 packs and of more, one row, and row counts on both sides of
+    half the CUs of an MI355X (128)."""
+    cs = [draw_wide(k) for k in range(WIDE_CASES)]
+    assert {c["dtype"] for c in cs} == set(DTYPES)
+    assert {c["ranks"] for c in cs} == set(range(1, 9))
+    packs = [c["hidden"] * (4 if c["dtype"] == "fp32" else 2) // 16 for c in cs]
+    assert any(p <= 4096 for p in packs) and any(p > 4096 for p in packs)
+    assert any(c["rows"] == 1 for c in cs)
+    wide = [c for c, p in zip(cs, packs) if p > 4096]
+    assert any(c["rows"] <= 128 for c in wide) and any(c["rows"] > 128 for c in wide)
+    assert {c["alias"] for c in cs} >= {"none", "out=partial", "inter=partial"}
