@@ -779,18 +779,27 @@ __global__ __launch_bounds__(kChunkLanes) void ar_rmsnorm_chunk_sum_kernel(Fused
     }
 }
 
-// Launch 2: one lane per row adds its chunks' sums of squares in chunk order
-// and writes the row's rstd into every chunk's head word.
+// Launch 2: one wave per row. Lane l loads the head words of chunks l, l+64,
+// ... (all loads in flight) and adds them in that order; the row's sum is
+// then the lanes' sums in lane order - chunk order whenever a row has at most
+// 64 chunks - and every lane writes the row's rstd back into its heads.
 __global__ __launch_bounds__(kWave) void ar_rmsnorm_row_scale_kernel(FusedArgs a, int chunks)
 {
-    const size_t stride = static_cast<size_t>(gridDim.x) * kWave;
-    for (size_t row = static_cast<size_t>(blockIdx.x) * kWave + threadIdx.x; row < a.rows; row += stride) {
+    const int lane = static_cast<int>(threadIdx.x);
+    const int used = chunks < kWave ? chunks : kWave;
+    for (size_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const size_t row0 = row * static_cast<size_t>(a.ppr);
-        float ss = *chunk_head(a, row0, 0);
-        for (int c = 1; c < chunks; ++c)
-            ss = ss + *chunk_head(a, row0, c);
+        float x = 0.0f;
+        if (lane < chunks) {
+            x = *chunk_head(a, row0, lane);
+            for (int c = lane + kWave; c < chunks; c += kWave)
+                x = x + *chunk_head(a, row0, c);
+        }
+        float ss = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+        for (int l = 1; l < used; ++l)
+            ss = ss + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
         const float rstd = rms_scale(ss, a.hidden, a.eps);
-        for (int c = 0; c < chunks; ++c)
+        for (int c = lane; c < chunks; c += kWave)
             *chunk_head(a, row0, c) = rstd;
     }
 }
@@ -1154,7 +1163,7 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
     } else if (vec && g.ppt == 0 && ar_geometry::wide_rows_chunked(a.ppr, a.rows, cus)) {
         const int chunks = (a.ppr + kChunkPacks - 1) / kChunkPacks;
         const unsigned cgrid = clamp_grid(a.rows * static_cast<size_t>(chunks));
-        const unsigned sgrid = clamp_grid((a.rows + kWave - 1) / kWave);
+        const unsigned sgrid = clamp_grid(a.rows);
         if (log_enabled())
             fprintf(stderr, "[ar] fused chunked R=%d rows=%zu H=%d ppr=%d chunks/row=%d block=%d grid=%u\n", R, a.rows,
                     a.hidden, a.ppr, chunks, kChunkLanes, cgrid);
