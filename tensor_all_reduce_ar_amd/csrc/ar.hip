@@ -33,10 +33,11 @@
 //    waves per workgroup where the width allows (the four SIMDs of a CU get
 //    equal shares), more lanes per row when there are too few rows to fill
 //    the chip;
-//  * rows wider than the register budget store S and read it back: one
-//    workgroup per row in two passes, or, when there are few such rows, one
-//    workgroup per 1024-pack chunk over three launches, the chunks' sums of
-//    squares passed through words of the output that are overwritten last.
+//  * rows wider than the register budget store S and read it back: past
+//    4096 packs one workgroup per 1024-pack chunk over three launches, the
+//    chunks' sums of squares passed through words of the output that are
+//    overwritten last; fp32 rows of 2049..4096 packs from 3 ranks one
+//    workgroup per row in two passes.
 // Shapes the vector path does not cover (pointers not 16-byte aligned, rows
 // whose byte size is not a multiple of 16, rows wider than the register
 // budget) run element-wise kernels with the same arithmetic.
@@ -726,8 +727,8 @@ __global__ __launch_bounds__(kWideThreads) void ar_rmsnorm_wide_kernel(FusedArgs
     }
 }
 
-// Rows of more than 4096 packs when there are few of them (no more than half
-// the CUs): one workgroup per chunk of kChunkPacks packs of a row
+// Rows of more than 4096 packs: one workgroup per chunk of kChunkPacks packs
+// of a row
 // (kChunkLanes lanes x 2 packs, all loads in flight), over three launches.
 // The chunks' sums of squares pass between the launches through the head
 // word (the first 4 bytes) of each chunk's region of `out`, which only the
@@ -1160,7 +1161,7 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
             ok = launch_fused_rows<E, R, 2>(a, g.threads, dev, cus, stream);
         if (!ok)
             return AR_ERR_SHAPE;  // unreachable: fused_geometry only yields shapes the kernel takes
-    } else if (vec && g.ppt == 0 && ar_geometry::wide_rows_chunked(a.ppr, a.rows, cus)) {
+    } else if (vec && g.ppt == 0 && ar_geometry::wide_rows_chunked(a.ppr)) {
         const int chunks = (a.ppr + kChunkPacks - 1) / kChunkPacks;
         const unsigned cgrid = clamp_grid(a.rows * static_cast<size_t>(chunks));
         const unsigned sgrid = clamp_grid(a.rows);

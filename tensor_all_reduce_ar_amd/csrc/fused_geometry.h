@@ -45,21 +45,22 @@ constexpr bool wide_rows_in_registers(int elem_size, int ranks)
     return elem_size == 2 || ranks <= kFp32WideRowMaxRanks;
 }
 
-// Rows of more than 4096 packs, when there are few of them: each row is cut
-// into chunks of kChunkPacks packs (kChunkLanes lanes x 2), one workgroup per
-// chunk, over three launches (sums, row scale, norm), so a few rows still
-// spread over the whole chip. Taken at no more rows than half the CUs: there
-// it measured 11-74 % faster than the two-pass kernel (1-128 rows of hidden
-// 40960..131072 in 16-bit types, 16388..65536 in fp32); at 192..819 rows the
-// two were within a few percent either way, the two-pass kernel ahead more
-// often. Narrower rows that still take the two-pass kernel (fp32 rows of
-// 2049..4096 packs from 3 ranks) keep it: there the two extra launches cost
-// more than the spread gains (18.6 % slower at 100 3-rank rows of 10240).
+// Rows of more than 4096 packs: each row is cut into chunks of kChunkPacks
+// packs (kChunkLanes lanes x 2), one workgroup per chunk, over three launches
+// (sums, row scale, norm), so the work spreads over the whole chip whatever
+// the row count. Against the two-pass kernel (one workgroup per row):
+// 11-74 % faster at 1-128 rows of hidden 40960..131072 in 16-bit types and
+// 16388..65536 in fp32, 4-9 % at 192-819 rows, within 2 % at 512-2048 8-rank
+// rows; 4-6 % slower only at 256 two-rank and 768 one-rank rows of 65536.
+// Narrower rows that take the two-pass kernel (fp32 rows of 2049..4096 packs
+// from 3 ranks) keep it: there the chunked path was 24 % slower on small
+// calls (100 3-rank rows of 10240) and 28 % faster on others, no better on
+// the whole.
 constexpr int kChunkLanes = 512;
 constexpr int kChunkPacks = 2 * kChunkLanes;
-inline bool wide_rows_chunked(int ppr, size_t rows, int cus)
+inline bool wide_rows_chunked(int ppr)
 {
-    return ppr > kMaxPPT * kWideRowLanes && rows * 2 <= static_cast<size_t>(cus);
+    return ppr > kMaxPPT * kWideRowLanes;
 }
 
 // How the one-row-per-workgroup kernel walks a lane's slots.

@@ -121,17 +121,15 @@ int main()
                 if (mode != kPlain && (ppt < 3 || (threads > kFullLanes && threads != kWideRowLanes)))
                     fail("pipeline_mode: pipelined walk outside the compiled shapes", ppr, false, false, none);
             }
-    // Rows of more than 4096 packs take the chunked path at no more rows than
-    // half the CUs, and only rows the register path does not hold in any
-    // type; a chunk is whole lanes x whole packs.
+    // Rows of more than 4096 packs take the chunked path - rows that no
+    // register path holds in any type; a chunk is whole lanes x whole packs.
     if (kChunkPacks % kChunkLanes != 0 || kChunkLanes % kWave != 0)
         fail("chunk shape", kChunkPacks, false, false, none);
-    for (int cus : {80, 104, 256, 304})
-        for (int ppr : {2049, 4096, 4097, 16384})
-            for (size_t rows : {size_t(1), size_t(cus / 2), size_t(cus / 2 + 1), size_t(cus)})
-                if (wide_rows_chunked(ppr, rows, cus) != (ppr > kMaxPPT * kWideRowLanes && rows * 2 <= size_t(cus)) ||
-                    (wide_rows_chunked(ppr, rows, cus) && fused_geometry(ppr, true, true).ppt != 0))
-                    fail("chunked-path rule", ppr, rows * 2 <= size_t(cus), true, none);
+    for (int ppr = 1; ppr <= 16384; ++ppr)
+        if (wide_rows_chunked(ppr) != (ppr > kMaxPPT * kWideRowLanes) ||
+            (wide_rows_chunked(ppr) && (fused_geometry(ppr, true, true).ppt != 0 ||
+                                        fused_geometry(ppr, false, true).ppt != 0)))
+            fail("chunked-path rule", ppr, false, true, none);
     // Which element types and rank counts take the 512-lane register path.
     for (int ranks = 1; ranks <= 8; ++ranks) {
         if (!wide_rows_in_registers(2, ranks))

@@ -226,8 +226,8 @@ def test_fused_widths(dtype, hidden):
     """Few rows: the register-row kernel in its latency layout (one pack per
     lane up to 1024 packs a row, two up to 2048), the 512-lane register path
     for rows of 2049..4096 packs (16-bit types, and fp32 at these two ranks),
-    the wide two-pass vector kernel past that, and the element kernel for rows
-    whose byte size is not a multiple of 16 (4100 fp16/bf16)."""
+    the chunked path past 4096 packs, and the element kernel for rows whose
+    byte size is not a multiple of 16 (4100 fp16/bf16)."""
     for rows in (1, 7, 33, 64):
         if rows * hidden > 1 << 21:
             continue
@@ -252,9 +252,9 @@ def test_fused_widths_at_the_layout_switch(dtype, hidden):
     covered, down to one lane: 1025 and 2047 packs) for the other rows of
     1025..2047 packs, 512 lanes with 5..8 packs (full or ragged) for rows of
     2049..4096 packs in 16-bit types, up to 512 lanes with 1..8 packs per
-    lane for the rest, and the two-pass wide kernel past that (fp32 rows of
-    more than 2048 packs at the 8 ranks used here, 16-bit rows of more than
-    4096). The row count at the switch and one past it."""
+    lane for the rest, and past that the two-pass kernel (fp32 rows of
+    2049..4096 packs at the 8 ranks used here) or the chunked path (rows of
+    more than 4096 packs). The row count at the switch and one past it."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for rows in (cus, cus + 1):
         note(f"[parity] fused {dtype} H={hidden} rows={rows} (CUs {cus})")
@@ -308,14 +308,13 @@ CHUNKED_CASES = [("bf16", 8, 32776), ("fp16", 2, 65536), ("bf16", 3, 131072), ("
 
 @pytest.mark.parametrize("dtype,ranks,hidden", CHUNKED_CASES)
 def test_fused_wide_rows_chunked(dtype, ranks, hidden):
-    """Rows of more than 4096 packs, at no more rows than half the CUs: one
-    workgroup per chunk of 1024 packs over three launches, the chunks' sums of
-    squares passed through the head words of the output. Widths with a short
-    last chunk (4097, 4098, 5121 and 5122 packs) and 8 and 16 whole chunks,
-    in every type. Row counts 1, 7 and half the CUs (chunked), and one more
-    (the two-pass kernel)."""
+    """Rows of more than 4096 packs: one workgroup per chunk of 1024 packs
+    over three launches, the chunks' sums of squares passed through the head
+    words of the output. Widths with a short last chunk (4097, 4098, 5121 and
+    5122 packs) and 8 and 16 whole chunks, in every type; 1, 7, half the CUs
+    and a few more than the CUs rows."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for rows in (1, 7, cus // 2, cus // 2 + 1):
+    for rows in (1, 7, cus // 2, cus + 3):
         if rows * hidden > 12 << 20:
             continue
         note(f"[parity] fused chunked {dtype} R={ranks} H={hidden} rows={rows} (CUs {cus})")

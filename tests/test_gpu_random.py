@@ -62,8 +62,8 @@ def device_with_offset(a, dtype, off):
 def draw_wide(case):
     """A fused case with rows of 2049..9000 16-byte packs - the 512-lane
     register path (fp32 up to 2 ranks, 16-bit types up to 4096 packs), the
-    two-pass kernel, and the chunked path (more than 4096 packs, no more rows
-    than half the CUs) - at 1..WIDE_MAX_ELEMS elements."""
+    two-pass kernel (fp32 rows of up to 4096 packs from 3 ranks) and the
+    chunked path (more than 4096 packs) - at 1..WIDE_MAX_ELEMS elements."""
     rng = np.random.Generator(np.random.PCG64(50_000 + case))
     c = {"op": "fused", "dtype": DTYPES[rng.integers(3)], "ranks": int(rng.integers(1, 9)), "seed": 60_000 + case}
     v = 4 if c["dtype"] == "fp32" else 8
@@ -165,13 +165,14 @@ def test_random_cases_cover_every_dimension():
 
 def test_random_wide_cases_cover_every_path():
     """Host only. The wide-row draw reaches every type and rank count, rows
-    of 2049..4096 packs and of more, one row, and row counts on both sides of
-    half the CUs of an MI355X (128)."""
+    of 2049..4096 packs (fp32 from 3 ranks among them) and of more, one row,
+    and rows wider than 4096 packs at more and fewer than 128 rows."""
     cs = [draw_wide(k) for k in range(WIDE_CASES)]
     assert {c["dtype"] for c in cs} == set(DTYPES)
     assert {c["ranks"] for c in cs} == set(range(1, 9))
     packs = [c["hidden"] * (4 if c["dtype"] == "fp32" else 2) // 16 for c in cs]
     assert any(p <= 4096 for p in packs) and any(p > 4096 for p in packs)
+    assert any(p <= 4096 and c["dtype"] == "fp32" and c["ranks"] >= 3 for c, p in zip(cs, packs))
     assert any(c["rows"] == 1 for c in cs)
     wide = [c for c, p in zip(cs, packs) if p > 4096]
     assert any(c["rows"] <= 128 for c in wide) and any(c["rows"] > 128 for c in wide)
