@@ -39,8 +39,8 @@
 //    overwritten last; fp32 rows of 2049..4096 packs from 3 ranks one
 //    workgroup per row in two passes.
 // Shapes the vector path does not cover (pointers not 16-byte aligned, rows
-// whose byte size is not a multiple of 16, rows wider than the register
-// budget) run element-wise kernels with the same arithmetic.
+// whose byte size is not a multiple of 16) run element-wise kernels with the
+// same arithmetic.
 
 #include <hip/hip_runtime.h>
 
@@ -728,12 +728,11 @@ __global__ __launch_bounds__(kWideThreads) void ar_rmsnorm_wide_kernel(FusedArgs
 }
 
 // Rows of more than 4096 packs: one workgroup per chunk of kChunkPacks packs
-// of a row
-// (kChunkLanes lanes x 2 packs, all loads in flight), over three launches.
-// The chunks' sums of squares pass between the launches through the head
-// word (the first 4 bytes) of each chunk's region of `out`, which only the
-// last launch overwrites, and only from the workgroup that reads it - so the
-// library still needs no scratch memory. Chunk c of a row covers packs
+// of a row (kChunkLanes lanes x 2 packs, all loads in flight), over three
+// launches. The chunks' sums of squares pass between the launches through the
+// head word (the first 4 bytes) of each chunk's region of `out`, which only
+// the last launch overwrites, and only from the workgroup that reads it - so
+// the library still needs no scratch memory. Chunk c of a row covers packs
 // c * kChunkPacks .. of that row.
 __device__ __forceinline__ float *chunk_head(const FusedArgs &a, size_t row0, int c)
 {
