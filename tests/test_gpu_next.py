@@ -145,6 +145,30 @@ def test_fused_slices_compose_to_the_full_op(dtype, num):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("num", [2, 4])
+def test_fused_slices_of_wide_rows(dtype, num):
+    """Slices of rows wider than 4096 packs (the chunked path: every row cut
+    into the same chunks whatever the slice) compose to the unsliced call
+    bit for bit, and match the oracle."""
+    hidden = 16388 * (1 if dtype == "fp32" else 2) * 2
+    w = inputs.random_fused(dtype, 3, 9, hidden, 1450 + num)
+    parts = [dev(p, dtype) for p in w.partials]
+    weight, bias, res = dev(w.weight, dtype), dev(w.bias, dtype), dev(w.residual, dtype)
+    out, inter = Guarded(w.n, dtype), Guarded(w.n, dtype)
+    for k in range(num):
+        ar.ar_residual_rmsnorm_slice(parts, weight, w.eps, out.t, inter.t, k, num, bias=bias, residual=res)
+    full_out, full_inter = torch.empty_like(parts[0]), torch.empty_like(parts[0])
+    ar.ar_residual_rmsnorm(parts, weight, w.eps, full_out, full_inter, bias=bias, residual=res)
+    torch.cuda.synchronize()
+    out.check_guards()
+    inter.check_guards()
+    ref_out, ref_inter = oracle_fused(w)
+    assert_bitexact(host_bits(inter.t), ref_inter, dtype, "wide-row slices intermediate")
+    assert_output_close(host_bits(out.t), ref_out, dtype, "wide-row slices output")
+    assert np.array_equal(host_bits(out.t), host_bits(full_out))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_prepared_slices_match_the_plain_slices(dtype):
     """Prepared slice calls (one per slice, on the current stream and on a
     side stream) write bitwise what the plain slice calls write, and the
