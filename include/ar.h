@@ -155,6 +155,11 @@ int32_t ar_sum(const ar_params_t *p, void *hip_stream);
  * Aliasing: the output and the intermediate may each equal a partial, and the
  * intermediate may equal the residual; outputs may not overlap each other,
  * bias or weight, and no partial overlap is allowed (AR_ERR_ALIAS).
+ * Rows of more than 4096 16-byte packs (hidden > 32768 in fp16/bf16, > 16384
+ * in fp32) run as three kernels on the stream, which pass each row's partial
+ * sums of squares through the first 4 bytes of every 1024-pack chunk of the
+ * output before writing the final values there; the output is meaningful,
+ * as always, only once the call's work on the stream has completed.
  */
 int32_t ar_residual_rmsnorm(const ar_params_t *p, void *hip_stream);
 
