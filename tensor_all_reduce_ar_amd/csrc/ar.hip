@@ -1061,14 +1061,15 @@ bool launch_fused_pack(const FusedArgs &a, unsigned grid, int threads, int dev, 
     }
 }
 
-// Rows of 2049..4096 packs in 16-bit types, and in fp32 with one or two
-// ranks: 512 lanes x PPT (5..8) packs in the pipelined variant, full or ragged
-// (one workgroup per CU: up to 230 VGPRs). Against the two-pass wide kernel
-// this measured 15-18 % faster on hidden 18432..32768 (bf16, 8 ranks), 2.4 %
-// on fp16 2-rank rows of 32768, and 5-30 % on fp32 one- and two-rank rows of
-// 9216..16384. Only these two forms are instantiated at this bound; fp32
-// rows of this width with more ranks keep the wide kernel (some of their
-// instances here would spill).
+// Rows of 2049..4096 packs in 16-bit types, and in fp32 where the instance
+// keeps everything in registers (ar_geometry::wide_rows_fit): 512 lanes x PPT
+// (5..8) packs in the pipelined variant, full or ragged (one workgroup per CU:
+// up to 253 VGPRs). Against the two-pass wide kernel this measured 15-18 %
+// faster on hidden 18432..32768 (bf16, 8 ranks), 2.4 % on fp16 2-rank rows of
+// 32768, 5-30 % on fp32 one- and two-rank rows of 9216..16384, and 7-12 % on
+// fp32 4- and 8-rank rows of 10240. Only these two forms are instantiated at
+// this bound, and in fp32 only the instances that fit; the other fp32 rows of
+// this width keep the wide kernel.
 // Returns false, launching nothing, unless the row needs exactly PPT slots of
 // kWideRowLanes lanes.
 template <class E, int R, int PPT>
@@ -1077,8 +1078,18 @@ bool launch_fused_pack_wide(const FusedArgs &a, unsigned grid, int threads, int 
     if (threads != kWideRowLanes)
         return false;
     switch (ar_geometry::pipeline_mode(PPT, threads, a.ppr)) {
-    case kFull: launch_fused_pack_as<E, R, PPT, kWideRowLanes, kFull>(a, grid, threads, dev, cus, stream); return true;
-    case kRagged: launch_fused_pack_as<E, R, PPT, kWideRowLanes, kRagged>(a, grid, threads, dev, cus, stream); return true;
+    case kFull:
+        if constexpr (ar_geometry::wide_rows_fit(E::kSize, R, PPT, false)) {
+            launch_fused_pack_as<E, R, PPT, kWideRowLanes, kFull>(a, grid, threads, dev, cus, stream);
+            return true;
+        }
+        return false;
+    case kRagged:
+        if constexpr (ar_geometry::wide_rows_fit(E::kSize, R, PPT, true)) {
+            launch_fused_pack_as<E, R, PPT, kWideRowLanes, kRagged>(a, grid, threads, dev, cus, stream);
+            return true;
+        }
+        return false;
     default: return false;
     }
 }
@@ -1138,7 +1149,7 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
         dev = current_device();
         cus = device_cus(dev);
         g = ar_geometry::fused_geometry(a.ppr, ar_geometry::latency_layout(a.ppr, a.rows, cus),
-                                        ar_geometry::wide_rows_in_registers(E::kSize, R));
+                                        ar_geometry::wide_rows_in_registers(E::kSize, R, a.ppr));
     }
     if (vec && g.waves > 0) {
         if (log_enabled())
@@ -1185,7 +1196,7 @@ int32_t launch_fused(const ar_params_t *p, hipStream_t stream, bool vec)
             default: break;
             }
         } else if (g.bound == kWideRowLanes && g.ppt > 2) {
-            if constexpr (ar_geometry::wide_rows_in_registers(E::kSize, R)) {
+            {
                 switch (g.ppt) {
                 case 5: ok = launch_fused_pack_wide<E, R, 5>(a, grid, t, dev, cus, stream); break;
                 case 6: ok = launch_fused_pack_wide<E, R, 6>(a, grid, t, dev, cus, stream); break;

@@ -34,15 +34,23 @@ constexpr int kRowsMaxPacks = 512;  // multi-row kernel: widest row, and workgro
 constexpr int kWideRowLanes = 512;  // register path for rows of 2049..4096 packs (16-bit types)
 constexpr int kWideThreads = 1024;  // workgroup size of the two-pass kernel for rows wider than that
 
-// Whether rows of 2049..4096 packs take the 512-lane register path: always in
-// 16-bit types, and in fp32 with up to kFp32WideRowMaxRanks ranks, whose
-// instances keep every value in registers at 5..8 packs per lane (101-230
-// VGPRs); from 3 ranks up some fp32 instances there spill, so those rows take
-// the two-pass wide kernel.
+// Whether the 512-lane register path has an instance for rows of 2049..4096
+// packs at `ppt` packs per lane (ragged: the last slot partly covered): every
+// one in 16-bit types, and in fp32 those that keep every value in registers -
+// all of them up to 2 ranks (101-230 VGPRs), and at 5 packs per lane every
+// rank count (152-253 VGPRs) except the 8-rank ragged walk, which spills. The
+// other fp32 ones spill (from 3 ranks at 7-8 packs, from 4 at 6-7, from 7 at
+// 6), so those rows take the two-pass wide kernel.
 constexpr int kFp32WideRowMaxRanks = 2;
-constexpr bool wide_rows_in_registers(int elem_size, int ranks)
+constexpr bool wide_rows_fit(int elem_size, int ranks, int ppt, bool ragged)
 {
-    return elem_size == 2 || ranks <= kFp32WideRowMaxRanks;
+    return elem_size == 2 || ranks <= kFp32WideRowMaxRanks || (ppt == 5 && (ranks <= 7 || !ragged));
+}
+
+// Whether a row of `ppr` packs (2049..4096) takes the 512-lane register path.
+constexpr bool wide_rows_in_registers(int elem_size, int ranks, int ppr)
+{
+    return wide_rows_fit(elem_size, ranks, (ppr + kWideRowLanes - 1) / kWideRowLanes, ppr % kWideRowLanes != 0);
 }
 
 // Rows of more than 4096 packs: each row is cut into chunks of kChunkPacks

@@ -1,8 +1,8 @@
 // Host check of the fused op's launch geometry (csrc/fused_geometry.h) for
-// every row width of 1..8192 packs, both layouts (few rows or many) and both
-// classes of element type and rank count (16-bit types, and fp32 with one or
-// two ranks, take the 512-lane register path for rows of 2049..4096 packs;
-// fp32 with more ranks does not). For each shape it checks what the
+// every row width of 1..8192 packs, both layouts (few rows or many), both
+// element sizes and every rank count (16-bit types take the 512-lane register
+// path for every row of 2049..4096 packs, fp32 only where its instance keeps
+// everything in registers). For each shape it checks what the
 // kernels assume: whole waves, no more lanes than the instance's launch
 // bound, lanes x packs covering the row, no lane slot that is empty for every
 // lane, a (packs per lane, launch bound, slot walk) combination that the
@@ -27,15 +27,16 @@ static void fail(const char *what, int ppr, bool few, bool wide, const FusedGeom
                     few, wide, g.ppt, g.threads, g.bound, g.rows, g.waves);
 }
 
-// The instances ar.hip compiles for the one-row-per-workgroup kernel.
-static bool instance_exists(int ppt, int bound, int mode, bool wide)
+// The instances ar.hip compiles for the one-row-per-workgroup kernel, for an
+// element size and rank count.
+static bool instance_exists(int ppt, int bound, int mode, int elem_size, int ranks)
 {
     if (bound == kFusedMaxThreads)
         return (ppt == 1 || ppt == 2) && mode == kPlain;
     if (bound == 512 && (ppt == 1 || ppt == 2))
         return mode == kPlain;
     if (bound == kWideRowLanes && ppt >= 5 && ppt <= kMaxPPT)
-        return wide && (mode == kFull || mode == kRagged);
+        return (mode == kFull || mode == kRagged) && wide_rows_fit(elem_size, ranks, ppt, mode == kRagged);
     if (bound == 256)
         return ppt >= 3 && ppt <= kMaxPPT && (mode == kFull || (mode == kRagged && ppt >= 5));
     return false;
@@ -46,7 +47,9 @@ int main()
     long checked = 0;
     for (int ppr = 1; ppr <= 8192; ++ppr) {
         for (int few = 0; few < 2; ++few) {
-            for (int wide = 0; wide < 2; ++wide) {
+            for (int cls = 0; cls < 16; ++cls) {
+                const int elem_size = cls < 8 ? 2 : 4, ranks = cls % 8 + 1;
+                const bool wide = wide_rows_in_registers(elem_size, ranks, ppr);
                 const FusedGeometry g = fused_geometry(ppr, few, wide);
                 ++checked;
                 const bool in_registers = ppr <= kMaxPPT * 256 || (wide && ppr <= kMaxPPT * kWideRowLanes);
@@ -78,7 +81,7 @@ int main()
                 if ((g.ppt - 1) * g.threads >= ppr)
                     fail("a slot empty for every lane", ppr, few, wide, g);
                 const int mode = pipeline_mode(g.ppt, g.threads, ppr);
-                if (!instance_exists(g.ppt, g.bound, mode, wide))
+                if (!instance_exists(g.ppt, g.bound, mode, elem_size, ranks))
                     fail("no compiled instance for this shape", ppr, few, wide, g);
                 if (mode == kFull && ppr != g.ppt * g.threads)
                     fail("full pipeline on a row that does not fill every slot", ppr, few, wide, g);
@@ -130,13 +133,17 @@ int main()
             (wide_rows_chunked(ppr) && (fused_geometry(ppr, true, true).ppt != 0 ||
                                         fused_geometry(ppr, false, true).ppt != 0)))
             fail("chunked-path rule", ppr, false, true, none);
-    // Which element types and rank counts take the 512-lane register path.
-    for (int ranks = 1; ranks <= 8; ++ranks) {
-        if (!wide_rows_in_registers(2, ranks))
-            fail("16-bit rows kept off the 512-lane register path", ranks, false, false, none);
-        if (wide_rows_in_registers(4, ranks) != (ranks <= kFp32WideRowMaxRanks))
-            fail("fp32 rank rule of the 512-lane register path", ranks, false, true, none);
-    }
+    // Which rows take the 512-lane register path: every 16-bit row of
+    // 2049..4096 packs; fp32 rows up to 2 ranks, and from 3 ranks only rows of
+    // 2049..2560 packs (5 per lane), at 8 ranks only the full ones.
+    for (int ranks = 1; ranks <= 8; ++ranks)
+        for (int ppr = 2049; ppr <= 4096; ++ppr) {
+            if (!wide_rows_in_registers(2, ranks, ppr))
+                fail("16-bit row kept off the 512-lane register path", ppr, false, false, none);
+            const bool fp32 = ranks <= kFp32WideRowMaxRanks || (ppr <= 2560 && (ranks <= 7 || ppr == 2560));
+            if (wide_rows_in_registers(4, ranks, ppr) != fp32)
+                fail("fp32 rule of the 512-lane register path", ppr, false, true, none);
+        }
     if (failures) {
         std::printf("%d failures\n", failures);
         return 1;

@@ -278,14 +278,17 @@ def test_fused_rows_at_the_latency_switch(dtype, hidden):
         check_fused(w, got_out, got_inter)
 
 
-@pytest.mark.parametrize("ranks", [1, 2, 3])
-@pytest.mark.parametrize("hidden", [8196, 8200, 9216, 10240, 12288, 14336, 16376, 16384])
+@pytest.mark.parametrize("ranks", [1, 2, 3, 7, 8])
+@pytest.mark.parametrize("hidden", [8196, 8200, 9216, 10240, 10244, 12288, 14336, 16376, 16384])
 def test_fp32_rows_of_2049_to_4096_packs(ranks, hidden):
-    """fp32 rows of 2049..4096 packs: with one or two ranks the 512-lane
-    register path (5..8 packs per lane, full, or ragged down to one lane in
-    the last slot at 8196), with three the two-pass wide kernel; a few rows
-    and more rows than CUs, then the same call with the intermediate written
-    over the residual and the output over the last partial."""
+    """fp32 rows of 2049..4096 packs: the 512-lane register path wherever its
+    instance fits in registers - every row up to 2 ranks (5..8 packs per lane,
+    full, or ragged down to one lane in the last slot at 8196), and rows of
+    up to 2560 packs at more ranks (at 8 ranks only the full 10240) - and the
+    two-pass wide kernel for the rest (10244 and wider from 3 ranks, the
+    ragged 8-rank rows); a few rows and more rows than CUs, then the same call
+    with the intermediate written over the residual and the output over the
+    last partial."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for rows in (3, cus + 1):
         note(f"[parity] fused fp32 R={ranks} H={hidden} rows={rows}")
