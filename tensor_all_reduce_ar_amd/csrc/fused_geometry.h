@@ -38,9 +38,11 @@ constexpr int kWideThreads = 1024;  // workgroup size of the two-pass kernel for
 // packs at `ppt` packs per lane (ragged: the last slot partly covered): every
 // one in 16-bit types, and in fp32 those that keep every value in registers -
 // all of them up to 2 ranks (101-230 VGPRs), and at 5 packs per lane every
-// rank count (152-253 VGPRs) except the 8-rank ragged walk, which spills. The
-// other fp32 ones spill (from 3 ranks at 7-8 packs, from 4 at 6-7, from 7 at
-// 6), so those rows take the two-pass wide kernel.
+// rank count (152-253 VGPRs) except the 8-rank ragged walk, which spills.
+// Most other fp32 ones spill too (every one at 7-8 packs from 4 ranks, at 6
+// packs from 7 ranks and in the 6-rank ragged walk, the 3-rank ragged walk
+// at 8); the few that do not are left out to keep this rule short, and those
+// rows take the two-pass wide kernel.
 constexpr int kFp32WideRowMaxRanks = 2;
 constexpr bool wide_rows_fit(int elem_size, int ranks, int ppt, bool ragged)
 {
